@@ -1,0 +1,13 @@
+"""fp64 CPU oracle for paged KV-cache attention.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check in the
+package entry file and by the CPU-baseline leg of the benchmark, never by the
+library or its binding. It shares no code with the HIP path.
+"""
+from .paged_attention import (  # noqa: F401
+    attend,
+    gather_sequence,
+    kv_store,
+    paged_attn_decode,
+    paged_attn_prefill,
+)
