@@ -1,0 +1,337 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+Headline workload (config 2, Qwen3-0.6B-shaped decode): one step = store the
+64 new tokens' K/V through slot_mapping, then paged decode attention of 64
+sequences (16 query / 8 KV heads, head_dim 128, bf16, contexts uniform in
+[128, 4096]) over 256-token blocks drawn from a shuffled pool.
+
+The timed region holds exactly --steps steps, bracketed by device
+synchronisation. Pool copies rotate between steps so that a step never finds
+the previous step's K/V in the 256 MB memory-side cache: every step reads its
+K/V from HBM. Per-kernel durations come from HIP events recorded on the stream
+the kernels are launched on.
+
+Printed: one JSON line with the headline value (decode-step KV throughput in
+TB/s), the roofline of the decode kernel, the fp64 CPU oracle timed on the
+host on a bounded sample, and secondary measurements of the other workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published (no sparsity)
+METRIC = "paged-attn decode KV TB/s (% HBM peak); prefill TFLOP/s (% MFMA peak)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "decode": os.path.join(ROOT, "paged_kv_cache_209_amd", "csrc", "decode.hip"),
+    "prefill": os.path.join(ROOT, "paged_kv_cache_209_amd", "csrc", "prefill.hip"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(kernel: str) -> str:
+    with open(KERNEL_SOURCES[kernel], "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    rec = data.get(f"{kernel}:{workload}")
+    if not rec or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def decode_bytes(case) -> dict:
+    """Algorithmic bytes of one decode launch: every K/V row of every context
+    once (shared prefix rows once), q and out, the block-table entries read,
+    and the context lengths."""
+    import workloads as w
+
+    elt = case.q.element_size()
+    hkv, d = case.num_kv_heads, case.head_dim
+    ctx = case.context_lens.tolist()
+    seen = set()
+    unique_rows = 0
+    for i, L in enumerate(ctx):
+        for b in range(w.blocks_for(L)):
+            blk = int(case.block_tables[i, b])
+            rows = min(256, L - 256 * b)
+            if blk in seen:
+                continue  # a shared block (same id) is read from HBM once
+            seen.add(blk)
+            unique_rows += rows
+    kv_row = hkv * d * elt * 2
+    logical = sum(ctx) * kv_row
+    qo = 2 * case.q.numel() * elt
+    meta = sum(w.blocks_for(L) for L in ctx) * 4 + len(ctx) * 4
+    return {"unique_kv": unique_rows * kv_row, "logical_kv": logical, "q_out": qo, "meta": meta,
+            "total": unique_rows * kv_row + qo + meta}
+
+
+def decode_flops(case) -> float:
+    return 4.0 * case.head_dim * case.num_q_heads * float(case.context_lens.sum())
+
+
+def prefill_flops(case) -> float:
+    cu = case.cu_seqlens.tolist()
+    tot = 0.0
+    for i, L in enumerate(case.context_lens.tolist()):
+        n = cu[i + 1] - cu[i]
+        c = L - n
+        tot += n * c + n * (n + 1) / 2
+    return 4.0 * case.head_dim * case.num_q_heads * tot
+
+
+def prefill_bytes(case) -> dict:
+    import workloads as w
+
+    elt = case.q.element_size()
+    hkv, d = case.num_kv_heads, case.head_dim
+    cu = case.cu_seqlens.tolist()
+    seen = set()
+    unique_rows = 0
+    logical = 0
+    for i, L in enumerate(case.context_lens.tolist()):
+        c = L - (cu[i + 1] - cu[i])
+        logical += c
+        for b in range(w.blocks_for(c)):
+            blk = int(case.block_tables[i, b])
+            if blk in seen:
+                continue
+            seen.add(blk)
+            unique_rows += min(256, c - 256 * b)
+    kv_row = hkv * d * elt * 2
+    new = case.total_q * (2 * case.num_q_heads + 2 * hkv) * d * elt  # q, out, k, v
+    meta = (len(cu) + case.num_seqs) * 4
+    return {"unique_kv": unique_rows * kv_row, "logical_kv": logical * kv_row, "new_tokens": new,
+            "total": unique_rows * kv_row + new + meta}
+
+
+class Timer:
+    """Pairs of HIP events on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append([e, None])
+
+    def stop(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[-1][1] = e
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+
+def run_decode_workload(torch, pa, case, steps, warmup, copies, with_store):
+    """Time `steps` decode steps (optionally with the store) on rotating pool copies."""
+    dev = "cuda:0"
+    kcs = [case.k_cache.to(dev)]
+    vcs = [case.v_cache.to(dev)]
+    for _ in range(copies - 1):
+        kcs.append(kcs[0].clone())
+        vcs.append(vcs[0].clone())
+    q = case.q.to(dev)
+    out = torch.empty_like(q)
+    bt = case.block_tables.to(dev)
+    cl = case.context_lens.to(dev)
+    if with_store:
+        kn, vn, sm = case.k_new.to(dev), case.v_new.to(dev), case.slot_mapping.to(dev)
+    maxc = case.max_context_len
+    ws = pa._lib.workspace(q.device, pa.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim, maxc))
+
+    def step(i, t_dec=None, t_store=None):
+        kc, vc = kcs[i % copies], vcs[i % copies]
+        if with_store:
+            if t_store:
+                t_store.start()
+            pa.kv_store(kc, vc, kn, vn, sm)
+            if t_store:
+                t_store.stop()
+        if t_dec:
+            t_dec.start()
+        pa.paged_attn_decode(out, q, kc, vc, bt, cl, case.scale, maxc, workspace_tensor=ws)
+        if t_dec:
+            t_dec.stop()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_dec, t_store, t_all = Timer(torch), Timer(torch), Timer(torch)
+    t0 = time.perf_counter()
+    t_all.start()
+    for i in range(steps):
+        step(warmup + i, t_dec, t_store if with_store else None)
+    t_all.stop()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    res = {"step_ms": t_all.ms()[0] / steps, "wall_ms": wall * 1e3 / steps, "decode_ms": t_dec.ms()}
+    if with_store:
+        res["store_ms"] = t_store.ms()
+    del kcs, vcs
+    torch.cuda.empty_cache()
+    return res
+
+
+def median(x):
+    s = sorted(x)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def cpu_baseline(case, budget_s: float):
+    """The fp64 oracle (unchanged) on the host cores, on whole decode steps of
+    the same workload (store + decode), repeated until `budget_s` has passed."""
+    import torch
+
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    nbytes = decode_bytes(case)["total"] + 2 * case.k_new.numel() * case.k_new.element_size() * 2
+    t0 = time.perf_counter()
+    seqs_done = 0
+    while time.perf_counter() - t0 < budget_s:
+        kc, vc = oracle.kv_store(case.k_cache, case.v_cache, case.k_new, case.v_new, case.slot_mapping)
+        for i in range(case.num_seqs):
+            oracle.paged_attn_decode(case.q, kc, vc, case.block_tables, case.context_lens, case.scale, seqs=[i])
+            seqs_done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    el = time.perf_counter() - t0
+    frac = seqs_done / case.num_seqs
+    value = nbytes * frac / el / 1e12
+    return {"value": value, "unit": "TB/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{seqs_done} sequences of the config-2 decode step (store + decode, {frac:.2f} steps) "
+                      f"in {el:.1f} s on {cores} host cores, fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=4, help="pool copies rotated between steps")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--skip-secondary", action="store_true")
+    ap.add_argument("--only", default="", help="run just one workload: c2 | c4 | c3 | c5 (profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the paged-attention kernels run on a single device and this "
+              "build has no multi-GPU path (per-GPU work would be sharded by sequence or KV head with no "
+              "exchange). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_209_amd as pa
+    import workloads as w
+
+    pa.library()
+    log(f"{pa.version()} on {torch.cuda.get_device_name(0)}")
+
+    secondary = {}
+    if args.only in ("", "c2"):
+        c2 = w.config2(device="cuda:0")
+        r = run_decode_workload(torch, pa, c2, args.steps, args.warmup, args.copies, with_store=True)
+        db = decode_bytes(c2)
+        store_bytes = 2 * 2 * c2.k_new.numel() * c2.k_new.element_size()  # read + write of k and v rows
+        step_bytes = db["total"] + store_bytes
+        dec_ms = sum(r["decode_ms"]) / len(r["decode_ms"])
+        value = step_bytes / (r["step_ms"] * 1e-3) / 1e12
+        achieved = db["total"] / (dec_ms * 1e-3) / 1e9
+        traffic = measured_traffic("decode", "c2")
+        result = {
+            "metric": METRIC,
+            "value": round(value, 4),
+            "unit": "TB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(r["step_ms"], 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {
+                "workload": "c2_qwen3_0.6b_decode_step: kv_store of 64 new tokens + paged decode, batch 64, "
+                            "16 Q / 8 KV heads, head_dim 128, 256-token blocks, contexts U[128,4096], bf16 "
+                            "inputs, fp32 accumulation",
+                "num_seqs": 64,
+                "total_context_tokens": int(c2.context_lens.sum()),
+                "decode_workgroups": pa.decode_num_workgroups(64, 16, 8, c2.max_context_len),
+                "pool_copies_rotated": args.copies,
+                "step_bytes": step_bytes,
+                "parallelism": "single GPU",
+            },
+            "roofline": {
+                "kernel": "paged_decode_kernel<bf16,128,2>",
+                "bound": "hbm",
+                "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "algorithmic_bytes_per_launch": db["total"],
+                "avg_launch_us": round(dec_ms * 1e3, 2),
+                "median_launch_us": round(median(r["decode_ms"]) * 1e3, 2),
+            },
+            "wall_ms_per_step": round(r["wall_ms"], 5),
+            "store_avg_us": round(sum(r["store_ms"]) / len(r["store_ms"]) * 1e3, 2),
+        }
+    else:
+        result = {"metric": METRIC, "value": None, "note": f"--only {args.only}"}
+
+    if not args.skip_secondary and args.only in ("", "c4"):
+        c4 = w.config4(device="cuda:0")
+        r4 = run_decode_workload(torch, pa, c4, max(5, args.steps // 5), 2, 1, with_store=False)
+        db4 = decode_bytes(c4)
+        ms = sum(r4["decode_ms"]) / len(r4["decode_ms"])
+        secondary["c4_qwen3_8b_decode_shared_prefix"] = {
+            "decode_avg_us": round(ms * 1e3, 1),
+            "unique_kv_TBps": round(db4["total"] / (ms * 1e-3) / 1e12, 4),
+            "frac_hbm_peak": round(db4["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "logical_kv_bytes": db4["logical_kv"],
+            "unique_bytes": db4["total"],
+            "decode_workgroups": pa.decode_num_workgroups(256, 32, 8, c4.max_context_len),
+        }
+        del c4
+        torch.cuda.empty_cache()
+
+    if secondary:
+        result["secondary"] = secondary
+    if not args.skip_cpu and args.only in ("", "c2"):
+        log("timing the fp64 oracle on the host ...")
+        result["cpu_baseline"] = cpu_baseline(w.config2(), args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * paged_attn.h -- C ABI of libpagedattn.so, paged KV-cache attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the attention layer of the Nano-vLLM engine as
+ * described on "Nano-vLLM System Architecture Analysis", section 2 "Core
+ * Components":
+ *   - "Paged KV Cache": the KV cache is split into fixed 256-token blocks
+ *     drawn from a free pool; blocks may be shared between sequences.
+ *   - "Attention with Paged Cache": computed K/V entries are stored into the
+ *     paged cache via slot_mapping; prefill with a prefix cache gathers cached
+ *     K/V and concatenates the newly computed ones; decode gathers all cached
+ *     K/V before attention.
+ * and section 3 "Lifecycle of a Request" (prepare_inputs builds block tables
+ * and slot mappings per step). Attention itself is softmax(q k^T * scale) v
+ * (Baidu article on Nano-vLLM, "TorchScript Optimization"), with grouped-query
+ * heads ("Differences from Normal nanoGPT Inference", item 6).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Layout. All tensors are dense and row-major, in device memory.
+ *   pools    k_cache, v_cache : [num_blocks, block_size, num_kv_heads, head_dim]
+ *            The token at logical position p of sequence i lives in block
+ *            block_tables[i][p / block_size], row p % block_size; its flat
+ *            slot is block_id * block_size + row.
+ *   block_tables : int32 [num_seqs, max_blocks_per_seq]; entries past
+ *            ceil(context_lens[i] / block_size) are never read (-1 by habit).
+ *   q / out  : decode [num_seqs, num_q_heads, head_dim];
+ *              prefill [total_q, num_q_heads, head_dim].
+ *   GQA      : query head g reads KV head g / (num_q_heads / num_kv_heads).
+ * Types. pa_dtype names the element type of q, k, v, the pools and out
+ *   (all the same). Accumulation is fp32; bf16 outputs are rounded to
+ *   nearest-even. Metadata is int32.
+ * Supported shapes. block_size == 256; head_dim in {64, 128};
+ *   num_q_heads % num_kv_heads == 0; num_blocks * block_size < 2^31.
+ * Streams. `stream` is a hipStream_t (NULL = the legacy default stream).
+ *   PA_OK means the work was enqueued on `stream`; it runs asynchronously.
+ * Ownership. The caller allocates and frees every buffer, including the
+ *   workspace. The library keeps no pointer after a call returns and
+ *   allocates no device memory.
+ * Errors. Each call validates its host-side arguments before touching the
+ *   device and returns a pa_status; nothing aborts or throws across the ABI.
+ *   Device-side metadata (block ids, slots, lengths) is the caller's
+ *   contract: out-of-range ids, duplicate slots or lengths beyond the table
+ *   are undefined behaviour, not detected errors.
+ * Threading. Calls are re-entrant. Calls that run concurrently (different
+ *   streams) must not share a workspace.
+ */
+#ifndef PAGED_ATTN_H_
+#define PAGED_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, non-positive or inconsistent size */
+  PA_ERR_UNSUPPORTED = -2, /* valid but not built: dtype, head_dim, block_size */
+  PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  PA_ERR_HIP = -4          /* the HIP runtime reported a launch error */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+typedef void* pa_stream_t; /* a hipStream_t */
+
+/* Library version string, e.g. "pagedattn 0.1.0 gfx950". Never NULL. */
+const char* pa_version(void);
+
+/* Human-readable name of a status code. Never NULL. */
+const char* pa_status_string(pa_status status);
+
+/*
+ * pa_kv_store -- scatter new K/V rows into the pools through slot_mapping.
+ *
+ * Defined by "Nano-vLLM System Architecture Analysis", section 2, "Attention
+ * with Paged Cache" (computed K/V entries are stored into the paged cache via
+ * slot_mapping) and section 3 (prepare_inputs builds the slot mappings).
+ *
+ * k, v         : [num_tokens, num_kv_heads, head_dim] in `dtype`, read only.
+ * slot_mapping : int32 [num_tokens]. Token t is copied, bit for bit, to flat
+ *                slot slot_mapping[t] of both pools; a negative entry means
+ *                the token is not stored.
+ * k_cache, v_cache : the pools, written only at the named slots.
+ * num_tokens == 0 is a valid no-op. Duplicate non-negative slots, or slots
+ * >= num_blocks * block_size, are undefined behaviour.
+ * Supported dtypes: PA_F32, PA_BF16.
+ */
+pa_status pa_kv_store(void* k_cache, void* v_cache, const void* k, const void* v,
+                      const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                      pa_stream_t stream);
+
+/*
+ * pa_paged_attn_decode -- one query token per sequence attending over its
+ * whole paged context.
+ *
+ * Defined by "Nano-vLLM System Architecture Analysis", section 2, "Attention
+ * with Paged Cache" (decode attends over all cached K/V of the sequence's
+ * blocks) and section 3 (decode produces one token per sequence per step).
+ * The K/V are streamed from the blocks in place; no gathered copy is made.
+ *
+ * out          : [num_seqs, num_q_heads, head_dim] in `dtype`, written.
+ * q            : [num_seqs, num_q_heads, head_dim] in `dtype`.
+ * context_lens : int32 [num_seqs], each in [1, max_context_len]; the count
+ *                includes the token stored in the same step. (A length
+ *                outside that range is a caller error: it is clamped to what
+ *                the block table holds and a non-positive one leaves that
+ *                sequence's output unwritten.)
+ * max_context_len : host-side upper bound of context_lens; must not exceed
+ *                max_blocks_per_seq * block_size.
+ * scale        : multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
+ * workspace    : device scratch of at least pa_decode_workspace_bytes(...)
+ *                bytes for the split-context partial results. Its first use
+ *                must see it zero-filled (e.g. from a zeroing allocation);
+ *                every completed call leaves its counter words zero again, so
+ *                the same workspace can be reused without clearing.
+ *                workspace may be NULL when max_context_len <= block_size
+ *                (pa_decode_workspace_bytes returns 0 then).
+ * Supported dtypes: PA_F32, PA_BF16.
+ */
+pa_status pa_paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                               int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                               pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                               pa_stream_t stream);
+
+/*
+ * pa_paged_attn_decode_ex -- pa_paged_attn_decode with an explicit number of
+ * workgroups (0 = the library's choice, the same as pa_paged_attn_decode).
+ * The decode work -- every 256-token block of every (sequence, query-head
+ * group) -- is cut into num_workgroups equal contiguous shares, so a long
+ * context may be split over several workgroups and merged afterwards.
+ * Results for one num_workgroups value are bit-identical from run to run;
+ * different values agree to rounding.
+ */
+pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                  pa_dtype dtype, int32_t num_workgroups, void* workspace,
+                                  size_t workspace_bytes, pa_stream_t stream);
+
+/* Number of workgroups pa_paged_attn_decode launches for these sizes. */
+int32_t pa_decode_num_workgroups(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t max_context_len);
+
+/*
+ * Workspace bytes that decode needs for these sizes with any number of
+ * workgroups (an upper bound; 0 when max_context_len fits in one block).
+ * max_q_len is ignored (decode has one query token per sequence).
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_q_len, int32_t max_context_len);
+
+/*
+ * pa_paged_attn_prefill -- causal attention of new tokens over each
+ * sequence's cached blocks followed by the new tokens themselves.
+ *
+ * Defined by "Nano-vLLM System Architecture Analysis", section 2, "Attention
+ * with Paged Cache" (prefill with a prefix cache gathers the cached K/V and
+ * concatenates the newly computed ones) and "Scheduler" (chunked prefill
+ * splits a long prompt over steps, so a chunk follows cached tokens). It also
+ * serves speculative verification, where the target model checks a few
+ * proposed tokens in one parallel mini-prefill ("What Is an Inference Engine,
+ * Anyway?", Technical details).
+ *
+ * q            : [total_q, num_q_heads, head_dim]; k, v : [total_q,
+ *                num_kv_heads, head_dim]: the new tokens' projections.
+ * cu_seqlens   : int32 [num_seqs + 1], cu_seqlens[0] = 0, non-decreasing,
+ *                cu_seqlens[num_seqs] = total_q. Sequence i owns rows
+ *                cu_seqlens[i] .. cu_seqlens[i+1]-1 (n_i <= max_q_len).
+ * context_lens : int32 [num_seqs] = cached + new tokens; the first
+ *                c_i = context_lens[i] - n_i positions come from the pools
+ *                through block_tables, the last n_i from k/v (the pools are
+ *                not read at those positions, whether or not they were stored).
+ * Causality    : new token j of sequence i (position c_i + j) attends to
+ *                positions 0 .. c_i + j.
+ * out          : [total_q, num_q_heads, head_dim], written.
+ * workspace    : as for decode, sized by pa_prefill_workspace_bytes; used
+ *                when short query chunks are split along the context.
+ * Supported dtypes: PA_BF16 (PA_F32 returns PA_ERR_UNSUPPORTED).
+ */
+pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const void* v,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_q,
+                                int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                pa_stream_t stream);
+
+/* Workspace bytes prefill needs for these sizes (an upper bound; may be 0). */
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_q_len, int32_t max_context_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H_ */

