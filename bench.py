@@ -198,6 +198,38 @@ def run_decode_workload(torch, pa, case, steps, warmup, copies, with_store):
     return res
 
 
+def run_prefill_workload(torch, pa, case, steps, warmup, with_store):
+    """Time `steps` prefill calls (each preceded by the store of the new tokens
+    when the case has a slot mapping)."""
+    dev = "cuda:0"
+    kc, vc = case.k_cache.to(dev), case.v_cache.to(dev)
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    out = torch.empty_like(q)
+    bt, cl, cu = case.block_tables.to(dev), case.context_lens.to(dev), case.cu_seqlens.to(dev)
+    sm = case.slot_mapping.to(dev) if with_store else None
+    mq, mc = case.max_q_len, case.max_context_len
+
+    def step(t=None):
+        if with_store:
+            pa.kv_store(kc, vc, k, v, sm)
+        if t:
+            t.start()
+        pa.paged_attn_prefill(out, q, k, v, kc, vc, bt, cl, cu, case.scale, mq, mc)
+        if t:
+            t.stop()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    for _ in range(steps):
+        step(t)
+    torch.cuda.synchronize()
+    del kc, vc
+    torch.cuda.empty_cache()
+    return t.ms()
+
+
 def median(x):
     s = sorted(x)
     n = len(s)
@@ -241,6 +273,8 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-secondary", action="store_true")
     ap.add_argument("--only", default="", help="run just one workload: c2 | c4 | c3 | c5 (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy --steps times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the paged-attention kernels run on a single device and this "
@@ -249,6 +283,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": args.steps}), flush=True)
+        return
 
     import paged_kv_cache_209_amd as pa
     import workloads as w
@@ -325,6 +368,38 @@ def main():
         del c4
         torch.cuda.empty_cache()
 
+    if not args.skip_secondary and args.only in ("", "c3"):
+        c3 = w.config3(device="cuda:0")
+        ms = run_prefill_workload(torch, pa, c3, max(10, args.steps), 3, with_store=True)
+        avg = sum(ms) / len(ms)
+        fl = prefill_flops(c3)
+        pb = prefill_bytes(c3)
+        secondary["c3_chunked_prefill_prefix_cache"] = {
+            "prefill_avg_us": round(avg * 1e3, 2),
+            "prefill_median_us": round(median(ms) * 1e3, 2),
+            "TFLOPs": round(fl / (avg * 1e-3) / 1e12, 2),
+            "frac_mfma_bf16_peak": round(fl / (avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops": fl,
+            "algorithmic_bytes": pb["total"],
+        }
+        del c3
+    if not args.skip_secondary and args.only in ("", "c5"):
+        c5 = w.config5(device="cuda:0")
+        ms = run_prefill_workload(torch, pa, c5, max(5, args.steps // 5), 2, with_store=False)
+        avg = sum(ms) / len(ms)
+        fl = prefill_flops(c5)
+        pb = prefill_bytes(c5)
+        secondary["c5_spec_verify"] = {
+            "verify_avg_us": round(avg * 1e3, 1),
+            "TBps": round(pb["total"] / (avg * 1e-3) / 1e12, 4),
+            "frac_hbm_peak": round(pb["total"] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOPs": round(fl / (avg * 1e-3) / 1e12, 2),
+            "frac_mfma_bf16_peak": round(fl / (avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops": fl,
+            "algorithmic_bytes": pb["total"],
+        }
+        del c5
+        torch.cuda.empty_cache()
     if secondary:
         result["secondary"] = secondary
     if not args.skip_cpu and args.only in ("", "c2"):

@@ -45,6 +45,9 @@
  *   are undefined behaviour, not detected errors.
  * Threading. Calls are re-entrant. Calls that run concurrently (different
  *   streams) must not share a workspace.
+ * Workspaces. Decode and prefill lay out their scratch differently: a
+ *   workspace zero-filled once may be reused by any number of calls of ONE
+ *   of the two entry points, never by both.
  */
 #ifndef PAGED_ATTN_H_
 #define PAGED_ATTN_H_

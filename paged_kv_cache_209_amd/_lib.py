@@ -115,10 +115,13 @@ def _dtype_code(t: torch.Tensor) -> int:
 _workspaces = {}
 
 
-def workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
+def workspace(device: torch.device, nbytes: int, kind: str = "decode") -> Optional[torch.Tensor]:
+    """Zero-filled scratch for one entry point ("decode" or "prefill") on one
+    device. The two entry points lay their counters out differently, so they
+    never share a buffer."""
     if nbytes == 0:
         return None
-    key = (device.type, device.index)
+    key = (device.type, device.index, kind)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
@@ -193,7 +196,7 @@ def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
     nb, bs, hkv, _ = k_cache.shape
     b = context_lens.shape[0]
     need = prefill_workspace_bytes(b, hq, d, max_q_len, max_context_len)
-    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need)
+    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need, "prefill")
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     status = library().pa_paged_attn_prefill(
         _ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),

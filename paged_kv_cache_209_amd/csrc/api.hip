@@ -39,6 +39,17 @@ size_t decode_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
   return pa::workspace_layout(num_seqs, num_q_heads, head_dim, 1, max_parts).total();
 }
 
+// Prefill workspace: one counter per (sequence, query head, query tile) bound
+// and two partial-result pieces per workgroup of the largest grid.
+pa::WorkspaceLayout prefill_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_q_len) {
+  pa::WorkspaceLayout w;
+  const int64_t counters = static_cast<int64_t>(num_seqs) * num_q_heads * (static_cast<int64_t>(max_q_len) + 1);
+  w.counters_bytes = static_cast<size_t>((counters * 4 + 255) / 256 * 256);
+  w.lse_bytes = static_cast<size_t>((pa::kPrefillSlotRows * 4 + 255) / 256 * 256);
+  w.out_bytes = static_cast<size_t>(pa::kPrefillSlotRows * head_dim * 4);
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -165,12 +176,8 @@ pa_status pa_paged_attn_decode(void* out, const void* q, const void* k_cache, co
 
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_q_len,
                                   int32_t max_context_len) {
-  (void)num_seqs;
-  (void)num_q_heads;
-  (void)head_dim;
-  (void)max_q_len;
-  (void)max_context_len;
-  return 0;
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_q_len <= 0 || max_context_len <= 0) return 0;
+  return prefill_layout(num_seqs, num_q_heads, head_dim, max_q_len).total();
 }
 
 pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const void* v, const void* k_cache,
@@ -180,31 +187,60 @@ pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const v
                                 int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                                 float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
                                 pa_stream_t stream) {
-  (void)out;
-  (void)q;
-  (void)k;
-  (void)v;
-  (void)k_cache;
-  (void)v_cache;
-  (void)block_tables;
-  (void)context_lens;
-  (void)cu_seqlens;
-  (void)num_seqs;
-  (void)total_q;
-  (void)max_q_len;
-  (void)num_q_heads;
-  (void)num_kv_heads;
-  (void)head_dim;
-  (void)block_size;
-  (void)num_blocks;
-  (void)max_blocks_per_seq;
-  (void)max_context_len;
-  (void)scale;
-  (void)dtype;
-  (void)workspace;
-  (void)workspace_bytes;
-  (void)stream;
-  return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_q_heads <= 0) return PA_ERR_INVALID_ARG;
+  const pa_status st = check_common(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (max_blocks_per_seq <= 0 || max_context_len <= 0) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return PA_ERR_INVALID_ARG;
+  if (max_q_len > max_context_len) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (k_cache == nullptr || v_cache == nullptr) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
+  if (out == nullptr || q == nullptr || k == nullptr || v == nullptr || block_tables == nullptr ||
+      context_lens == nullptr || cu_seqlens == nullptr)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return PA_ERR_INVALID_ARG;
+  const pa::WorkspaceLayout lay = prefill_layout(num_seqs, num_q_heads, head_dim, max_q_len);
+  if (workspace == nullptr || workspace_bytes < lay.total()) return PA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
+
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int32_t rows = static_cast<int64_t>(max_q_len) * group <= 32 ? 32 : 128;
+  const int64_t qtiles = ceil_div(static_cast<int64_t>(max_q_len) * group, rows);
+  const int64_t max_units = static_cast<int64_t>(num_seqs) * num_kv_heads * qtiles * ceil_div(max_context_len, 64);
+  const int64_t cap = rows == 128 ? pa::kPrefillMaxWorkgroups128 : pa::kPrefillMaxWorkgroups32;
+
+  pa::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.scale_log2 = scale * kLog2e;
+  a.rows_per_tile = rows;
+  a.num_workgroups = static_cast<int32_t>(max_units < cap ? max_units : cap);
+  char* ws = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<int32_t*>(ws);
+  a.part_lse = reinterpret_cast<float*>(ws + lay.counters_bytes);
+  a.part_out = reinterpret_cast<float*>(ws + lay.counters_bytes + lay.lse_bytes);
+  (void)hipGetLastError();
+  return to_status(pa::launch_prefill(a, head_dim, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

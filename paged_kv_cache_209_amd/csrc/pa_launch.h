@@ -55,12 +55,18 @@ struct PrefillArgs {
   int32_t max_blocks_per_seq;
   int32_t max_context_len;
   float scale_log2;
-  int32_t partition;  // context tokens per split work item (0 = no split)
-  int32_t max_parts;
-  int32_t* counters;
-  float* part_lse;
-  float* part_out;
+  int32_t rows_per_tile;   // query rows per item: 128 (4 waves) or 32 (1 wave)
+  int32_t num_workgroups;  // the key tiles of all items are split evenly over these
+  int32_t* counters;       // [num_seqs * num_q_heads * (max_q_len + 1)], zero between calls
+  float* part_lse;         // [2 * num_workgroups * rows_per_tile]
+  float* part_out;         // [2 * num_workgroups * rows_per_tile * head_dim]
 };
+
+// Largest grids the prefill launcher uses for each tile height, and the
+// partial-result rows their workspace holds (two pieces per workgroup).
+constexpr int kPrefillMaxWorkgroups128 = 512;
+constexpr int kPrefillMaxWorkgroups32 = 1024;
+constexpr int64_t kPrefillSlotRows = 2 * 512 * 128;
 
 hipError_t launch_prefill(const PrefillArgs& args, int32_t head_dim, hipStream_t stream);
 

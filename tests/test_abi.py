@@ -108,7 +108,19 @@ def pre(**kw):
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(dt=pa.PA_F32), UNSUP), (dict(d=96), UNSUP), (dict(bs=64), UNSUP),
+    (dict(dt=pa.PA_F32), UNSUP), (dict(d=96), UNSUP), (dict(bs=64), UNSUP), (dict(dt=9), INVALID),
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(cu=None), INVALID), (dict(vc=None), INVALID),
+    (dict(hq=6, hkv=4), INVALID), (dict(mq=5000), INVALID), (dict(mc=4097), INVALID), (dict(B=-1), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(v=P + 2), INVALID),
+    (dict(ws=None), WS), (dict(ws=P, wsb=4096), WS),
 ])
 def test_prefill_validation(kw, expect):
     assert pre(**kw) == expect
+
+
+def test_prefill_empty_is_noop_and_workspace_sizing():
+    assert pre(tq=0, out=None, q=None, k=None, v=None) == pa.PA_OK
+    assert pre(B=0) == pa.PA_OK
+    need = pa.prefill_workspace_bytes(2, 8, 128, 5, 4096)
+    assert need > 0
+    assert pre(ws=P, wsb=need - 16) == WS
