@@ -329,7 +329,7 @@ def main():
                             "inputs, fp32 accumulation",
                 "num_seqs": 64,
                 "total_context_tokens": int(c2.context_lens.sum()),
-                "decode_workgroups": pa.decode_num_workgroups(64, 16, 8, c2.max_context_len),
+                "decode_workgroups": pa.decode_num_workgroups(64, 16, 8, 128, c2.max_context_len),
                 "pool_copies_rotated": args.copies,
                 "step_bytes": step_bytes,
                 "parallelism": "single GPU",
@@ -363,7 +363,7 @@ def main():
             "frac_hbm_peak": round(db4["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "logical_kv_bytes": db4["logical_kv"],
             "unique_bytes": db4["total"],
-            "decode_workgroups": pa.decode_num_workgroups(256, 32, 8, c4.max_context_len),
+            "decode_workgroups": pa.decode_num_workgroups(256, 32, 8, 128, c4.max_context_len),
         }
         del c4
         torch.cuda.empty_cache()

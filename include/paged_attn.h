@@ -151,9 +151,15 @@ pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache,
                                   pa_dtype dtype, int32_t num_workgroups, void* workspace,
                                   size_t workspace_bytes, pa_stream_t stream);
 
-/* Number of workgroups pa_paged_attn_decode launches for these sizes. */
+/*
+ * Number of workgroups pa_paged_attn_decode launches for these sizes on the
+ * current device: as many as are resident at once (occupancy per compute unit
+ * times compute units), capped by the number of work units. 0 for sizes the
+ * library does not support. Queries the HIP runtime (falls back to 256 compute
+ * units when no device is visible).
+ */
 int32_t pa_decode_num_workgroups(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t max_context_len);
+                                 int32_t head_dim, int32_t max_context_len, pa_dtype dtype);
 
 /*
  * Workspace bytes that decode needs for these sizes with any number of

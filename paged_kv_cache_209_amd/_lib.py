@@ -41,7 +41,7 @@ SIGNATURES = {
                                     _f32, _i32, _vp, _sz, _vp]),
     "pa_paged_attn_decode_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
-    "pa_decode_num_workgroups": (_i32, [_i32, _i32, _i32, _i32]),
+    "pa_decode_num_workgroups": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
@@ -145,8 +145,10 @@ def kv_store(k_cache: torch.Tensor, v_cache: torch.Tensor, k: torch.Tensor, v: t
                                  hkv, d, bs, nb, _dtype_code(k_cache), _stream(k_cache)), "pa_kv_store")
 
 
-def decode_num_workgroups(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_context_len: int) -> int:
-    return int(library().pa_decode_num_workgroups(num_seqs, num_q_heads, num_kv_heads, max_context_len))
+def decode_num_workgroups(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_context_len: int,
+                          dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(library().pa_decode_num_workgroups(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                                  _DTYPES[dtype]))
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int) -> int:

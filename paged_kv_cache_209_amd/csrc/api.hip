@@ -13,9 +13,6 @@ namespace {
 
 constexpr int32_t kBlockSize = 256;
 constexpr float kLog2e = 1.4426950408889634f;
-// Decode workgroups launched by default: about four resident per compute unit
-// of an MI355X (256 CUs), each streaming an equal share of the KV blocks.
-constexpr int64_t kDecodeWorkgroups = 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -32,6 +29,13 @@ pa_status check_common(int32_t num_kv_heads, int32_t head_dim, int32_t block_siz
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 pa_status to_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// Upper bound of decode work units: one per 256-token block of the longest
+// context, for every (sequence, query-head group).
+int64_t decode_max_units(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len) {
+  const int64_t head_groups = num_q_heads / pa::decode_head_group(num_q_heads / num_kv_heads);
+  return static_cast<int64_t>(num_seqs) * head_groups * ceil_div(max_context_len, kBlockSize);
+}
 
 size_t decode_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= kBlockSize) return 0;
@@ -89,14 +93,14 @@ pa_status pa_kv_store(void* k_cache, void* v_cache, const void* k, const void* v
                                        static_cast<hipStream_t>(stream)));
 }
 
-int32_t pa_decode_num_workgroups(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t max_context_len) {
+int32_t pa_decode_num_workgroups(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_context_len, pa_dtype dtype) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len <= 0 ||
-      num_q_heads % num_kv_heads != 0)
-    return 1;
-  const int64_t head_groups = num_q_heads / pa::decode_head_group(num_q_heads / num_kv_heads);
-  const int64_t max_units = static_cast<int64_t>(num_seqs) * head_groups * ceil_div(max_context_len, kBlockSize);
-  return static_cast<int32_t>(max_units < kDecodeWorkgroups ? max_units : kDecodeWorkgroups);
+      num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128) || (dtype != PA_F32 && dtype != PA_BF16))
+    return 0;
+  const int32_t group = num_q_heads / num_kv_heads;
+  return pa::decode_default_workgroups(dtype == PA_BF16 ? pa::Dtype::kBF16 : pa::Dtype::kF32, head_dim, group,
+                                       decode_max_units(num_seqs, num_q_heads, num_kv_heads, max_context_len));
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_q_len,
@@ -126,14 +130,11 @@ pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache,
   if (out == nullptr || q == nullptr || block_tables == nullptr || context_lens == nullptr) return PA_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID_ARG;
 
-  const int32_t wgs = num_workgroups > 0
-                          ? num_workgroups
-                          : pa_decode_num_workgroups(num_seqs, num_q_heads, num_kv_heads, max_context_len);
   const int64_t max_parts = ceil_div(max_context_len, kBlockSize);
   pa::WorkspaceLayout lay = pa::workspace_layout(num_seqs, num_q_heads, head_dim, 1, max_parts);
   // An item is split over workgroups only if some workgroup gets less than a
   // whole item; with one block per context nothing is ever split.
-  const bool split = max_parts > 1 && wgs > 1;
+  const bool split = max_parts > 1 && num_workgroups != 1;
   if (split) {
     if (workspace == nullptr || workspace_bytes < lay.total()) return PA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
@@ -151,7 +152,8 @@ pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache,
   a.num_kv_heads = num_kv_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
-  a.num_workgroups = wgs;
+  a.num_workgroups = num_workgroups;  // 0: one resident round, chosen by the launcher
+  a.max_units = decode_max_units(num_seqs, num_q_heads, num_kv_heads, max_context_len);
   a.max_parts = static_cast<int32_t>(max_parts);
   a.scale_log2 = scale * kLog2e;
   char* ws = static_cast<char*>(workspace);

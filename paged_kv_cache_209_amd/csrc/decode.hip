@@ -85,7 +85,10 @@ __device__ __forceinline__ void load_row(const T* row, int sl, uint32_t (&w)[Dec
   using S = DecodeShape<T, D>;
 #pragma unroll
   for (int v = 0; v < S::kVecs; ++v) {
-    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(row + v * S::kVecStride + sl * S::kElemsPerVec);
+    // Streaming (non-temporal) loads: every K/V byte is used once, and on
+    // MI355X they sustain about 10% more bandwidth than cached loads.
+    const u32x4_t x =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + v * S::kVecStride + sl * S::kElemsPerVec));
     w[4 * v + 0] = x[0];
     w[4 * v + 1] = x[1];
     w[4 * v + 2] = x[2];
@@ -142,21 +145,46 @@ struct Chunk {
 
 template <typename T, int D>
 __device__ __forceinline__ void load_chunk(Chunk<DecodeShape<T, D>::kWords>& c, const T* kpool, const T* vpool,
-                                           const int32_t* table, int64_t row_stride, int c0, int t_end, int ts,
-                                           int sl) {
-  const int block = table[c0 / kTokensPerBlock];
-  const int ta = c0 + ts;
-  const int tb = c0 + 8 + ts;
+                                           int block, int64_t row_stride, int c0, int t_end, int ts, int sl) {
+  // Wave-uniform base of the chunk's first row plus a small per-lane offset.
   // Rows past the range are never read: their lanes re-read the last valid
   // row (always in the same block as the chunk start) and get zero weight.
-  const int ra = (ta < t_end ? ta : t_end - 1) % kTokensPerBlock;
-  const int rb = (tb < t_end ? tb : t_end - 1) % kTokensPerBlock;
-  const int64_t r0 = static_cast<int64_t>(block) * kTokensPerBlock;
-  load_row<T, D>(kpool + (r0 + ra) * row_stride, sl, c.ka);
-  load_row<T, D>(kpool + (r0 + rb) * row_stride, sl, c.kb);
-  load_row<T, D>(vpool + (r0 + ra) * row_stride, sl, c.va);
-  load_row<T, D>(vpool + (r0 + rb) * row_stride, sl, c.vb);
+  const int64_t r0 = static_cast<int64_t>(block) * kTokensPerBlock + (c0 % kTokensPerBlock);
+  const T* kb = kpool + r0 * row_stride;
+  const T* vb = vpool + r0 * row_stride;
+  const int last = t_end - 1 - c0;
+  const int rs = static_cast<int>(row_stride);
+  const int oa = min(ts, last) * rs;
+  const int ob = min(ts + 8, last) * rs;
+  load_row<T, D>(kb + oa, sl, c.ka);
+  load_row<T, D>(kb + ob, sl, c.kb);
+  load_row<T, D>(vb + oa, sl, c.va);
+  load_row<T, D>(vb + ob, sl, c.vb);
 }
+
+// Block ids of a segment, one per lane, 64 at a time. Each chunk takes its id
+// with a lane read (no memory wait), so block-table reads never sit in the
+// in-order queue of vector loads behind the K/V stream.
+struct BlockWindow {
+  const int32_t* table;
+  int base;   // first block index held
+  int limit;  // one past the segment's last block index
+  int id;     // this lane's block id: table[base + lane]
+  __device__ __forceinline__ void fill(int b, int lane) {
+    base = b;
+    id = b + lane < limit ? table[b + lane] : 0;
+    // Complete the load here, on this (rare) path, so that no later
+    // instruction inherits a pending table read and waits for the whole
+    // queue of K/V loads in front of it.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+  __device__ __forceinline__ int get(int b, int lane) {
+    if (b - base >= kWave) fill(b - (b - base) % kWave, lane);  // wave-uniform, rare
+    return __builtin_amdgcn_readlane(id, b - base);
+  }
+};
 
 template <typename T, int D, int GT>
 __device__ __forceinline__ void consume_chunk(LaneState<GT, DecodeShape<T, D>::kLaneElems>& st,
@@ -241,7 +269,9 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // wave index made provably wave-uniform, so per-wave addresses (block-table
+  // entries) are scalar loads that do not queue behind the vector loads
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int ts = lane >> 3;  // token slot within a chunk (and ts + 8)
   const int sl = lane & 7;   // sub-lane: which 16-byte pieces of the row
   const int B = a.num_seqs;
@@ -266,7 +296,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     s_scan[tid] += v;
     __syncthreads();
   }
-  const int64_t U = static_cast<int64_t>(HG) * s_scan[kDecodeThreads - 1];
+  const int64_t U = static_cast<int64_t>(HG) * __builtin_amdgcn_readfirstlane(s_scan[kDecodeThreads - 1]);
   // With no more workgroups than units every workgroup owns at least one
   // unit, so the owners of an item's units are consecutive workgroups.
   const int64_t G = min(static_cast<int64_t>(gridDim.x), U);
@@ -295,8 +325,10 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     }
   }
   __syncthreads();
-  int seq = s_loc[0];
-  int64_t seq_base = static_cast<int64_t>(HG) * s_loc[1];  // first unit of seq
+  // Values read back from LDS are uniform; say so, so that the whole walk
+  // (and every block-table lookup) stays in scalar registers.
+  int seq = __builtin_amdgcn_readfirstlane(s_loc[0]);
+  int64_t seq_base = static_cast<int64_t>(HG) * __builtin_amdgcn_readfirstlane(s_loc[1]);  // first unit of seq
 
   const int64_t row_stride = static_cast<int64_t>(a.num_kv_heads) * D;
   const float sc = a.scale_log2;
@@ -306,8 +338,9 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
   // ---- 3. Walk the segments (pieces of items) in [u_begin, u_end).
   int64_t u = u_begin;
   while (u < u_end) {
-    const int nb = context_blocks(a.context_lens[seq], a.max_context_len);
-    const int ctx = min(a.context_lens[seq], a.max_context_len);
+    const int ctx_raw = __builtin_amdgcn_readfirstlane(a.context_lens[seq]);
+    const int nb = context_blocks(ctx_raw, a.max_context_len);
+    const int ctx = min(ctx_raw, a.max_context_len);
     const int64_t r = u - seq_base;
     const int hg = static_cast<int>(r / nb);
     const int b_lo = static_cast<int>(r % nb);
@@ -326,26 +359,37 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     for (int g = 0; g < GT; ++g) load_row<T, D>(qbase + g * D, sl, qw[g]);
     const T* kpool = static_cast<const T*>(a.k_cache) + static_cast<int64_t>(kvh) * D;
     const T* vpool = static_cast<const T*>(a.v_cache) + static_cast<int64_t>(kvh) * D;
-    const int32_t* table = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks_per_seq;
+    BlockWindow bw;
+    bw.table = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks_per_seq;
+    bw.limit = b_hi;
+    bw.fill(b_lo, lane);
 
     // The 4 waves take 16-token chunks round-robin; each wave keeps the next
     // chunk's loads in flight while it works on the current one.
     st.reset();
     {
+      // The next chunk's loads are always issued (past the end they re-read
+      // the wave's last chunk, which the L2 still holds), so the number of
+      // loads in flight at each consume is the same on every path and the
+      // wait before it covers only the chunk being consumed.
       constexpr int kStride = kDecodeWaves * kChunk;
       int c0 = t_lo + wave * kChunk;
-      Chunk<W> cur, nxt;
-      if (c0 < t_hi) load_chunk<T, D>(cur, kpool, vpool, table, row_stride, c0, t_hi, ts, sl);
-      while (c0 < t_hi) {
-        const int c1 = c0 + kStride;
-        if (c1 < t_hi) load_chunk<T, D>(nxt, kpool, vpool, table, row_stride, c1, t_hi, ts, sl);
-        consume_chunk<T, D, GT>(st, cur, qw, c0 + ts < t_hi, c0 + 8 + ts < t_hi, sc);
-        c0 = c1;
-        if (c0 >= t_hi) break;
-        const int c2 = c0 + kStride;
-        if (c2 < t_hi) load_chunk<T, D>(cur, kpool, vpool, table, row_stride, c2, t_hi, ts, sl);
-        consume_chunk<T, D, GT>(st, nxt, qw, c0 + ts < t_hi, c0 + 8 + ts < t_hi, sc);
-        c0 = c2;
+      if (c0 < t_hi) {
+        const int c_last = c0 + (t_hi - 1 - c0) / kStride * kStride;
+        Chunk<W> cur, nxt;
+        load_chunk<T, D>(cur, kpool, vpool, bw.get(c0 / kTokensPerBlock, lane), row_stride, c0, t_hi, ts, sl);
+        while (true) {
+          int cn = min(c0 + kStride, c_last);
+          load_chunk<T, D>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, t_hi, ts, sl);
+          consume_chunk<T, D, GT>(st, cur, qw, c0 + ts < t_hi, c0 + 8 + ts < t_hi, sc);
+          c0 += kStride;
+          if (c0 >= t_hi) break;
+          cn = min(c0 + kStride, c_last);
+          load_chunk<T, D>(cur, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, t_hi, ts, sl);
+          consume_chunk<T, D, GT>(st, nxt, qw, c0 + ts < t_hi, c0 + 8 + ts < t_hi, sc);
+          c0 += kStride;
+          if (c0 >= t_hi) break;
+        }
       }
     }
 
@@ -443,15 +487,32 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     if (u == item_end && hg == HG - 1) {  // next sequence with work
       seq_base = item_end;
       ++seq;
-      while (u < u_end && seq < B - 1 && context_blocks(a.context_lens[seq], a.max_context_len) == 0) ++seq;
+      while (u < u_end && seq < B - 1 &&
+             context_blocks(__builtin_amdgcn_readfirstlane(a.context_lens[seq]), a.max_context_len) == 0)
+        ++seq;
     }
   }
 }
 
 template <typename T, int D, int GT>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  paged_decode_kernel<T, D, GT><<<dim3(static_cast<uint32_t>(a.num_workgroups)), dim3(kDecodeThreads), 0, stream>>>(a);
+  int wgs = a.num_workgroups;
+  if (wgs <= 0) wgs = resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, GT>),
+                                          kDecodeThreads, a.max_units);
+  paged_decode_kernel<T, D, GT><<<dim3(static_cast<uint32_t>(wgs)), dim3(kDecodeThreads), 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+int default_grid(int group, int64_t max_units) {
+  switch (decode_head_group(group)) {
+    case 4:
+      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 4>), kDecodeThreads, max_units);
+    case 2:
+      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 2>), kDecodeThreads, max_units);
+    default:
+      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 1>), kDecodeThreads, max_units);
+  }
 }
 
 template <typename T, int D>
@@ -475,6 +536,12 @@ hipError_t launch_decode(const DecodeArgs& a, Dtype dtype, int32_t head_dim, hip
   }
   if (head_dim == 128) return launch_group<float, 128>(a, stream);
   return launch_group<float, 64>(a, stream);
+}
+
+int decode_default_workgroups(Dtype dtype, int32_t head_dim, int32_t group, int64_t max_units) {
+  if (dtype == Dtype::kBF16) return head_dim == 128 ? default_grid<bf16_t, 128>(group, max_units)
+                                                    : default_grid<bf16_t, 64>(group, max_units);
+  return head_dim == 128 ? default_grid<float, 128>(group, max_units) : default_grid<float, 64>(group, max_units);
 }
 
 }  // namespace pa

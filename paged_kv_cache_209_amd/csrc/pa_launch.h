@@ -23,7 +23,8 @@ struct DecodeArgs {
   int32_t num_kv_heads;
   int32_t max_blocks_per_seq;
   int32_t max_context_len;
-  int32_t num_workgroups;  // the context work is split evenly over this many
+  int32_t num_workgroups;  // the context work is split evenly over this many (0: one resident round)
+  int64_t max_units;       // upper bound of the work units (the grid never exceeds it)
   int32_t max_parts;       // row stride of the partial-result arrays
   float scale_log2;   // scale * log2(e): scores are kept in base-2 units
   int32_t* counters;  // [num_seqs * num_q_heads], zero between calls
@@ -32,6 +33,14 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& args, Dtype dtype, int32_t head_dim, hipStream_t stream);
+
+// Grid the decode launcher uses when the caller does not fix one.
+int decode_default_workgroups(Dtype dtype, int32_t head_dim, int32_t group, int64_t max_units);
+
+// Workgroups of `kernel` (with `threads` per workgroup) that are resident on
+// the current device at once: occupancy per compute unit times compute units,
+// capped by `max_units` (queried once per kernel and device, then cached).
+int resident_workgroups(const void* kernel, int threads, int64_t max_units);
 
 // Query heads handled together by one decode workgroup (they share one KV
 // head's rows): the largest of 4, 2, 1 that divides the GQA group size.

@@ -142,7 +142,9 @@ __global__ __launch_bounds__(64 * WM) void paged_prefill_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // wave index made provably wave-uniform, so per-wave addresses (block-table
+  // entries) are scalar loads that do not queue behind the vector loads
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int col = lane & 15;  // MFMA column (query) / row-in-tile index
   const int grp = lane >> 4;  // MFMA lane group (k sub-block)
   const int B = a.num_seqs;
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(64 * WM) void paged_prefill_kernel(PrefillArgs a) {
     s_scan[tid] += v;
     __syncthreads();
   }
-  const int64_t U = s_scan[NT - 1];
+  const int64_t U = __builtin_amdgcn_readfirstlane(s_scan[NT - 1]);
   if (U == 0) return;
   const int64_t G = min(static_cast<int64_t>(gridDim.x), U);
   const int w = blockIdx.x;
@@ -190,8 +192,10 @@ __global__ __launch_bounds__(64 * WM) void paged_prefill_kernel(PrefillArgs a) {
     }
   }
   __syncthreads();
-  int seq = s_loc[0];
-  int64_t seq_base = s_loc[1];
+  // Values read back from LDS are uniform; say so, so that the walk and the
+  // block-table lookups stay in scalar registers.
+  int seq = __builtin_amdgcn_readfirstlane(s_loc[0]);
+  int64_t seq_base = __builtin_amdgcn_readfirstlane(s_loc[1]);
 
   const bf16_t* qg = static_cast<const bf16_t*>(a.q);
   const bf16_t* kg = static_cast<const bf16_t*>(a.k);

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import paged_kv_cache_209_amd as pa
 from paged_kv_cache_209_amd import _lib
@@ -93,9 +94,10 @@ def test_decode_workspace_sizing():
     assert need >= 4 * 8 * 16 * (128 + 1) * 4
     assert dec(ws=P, wsb=need - 1) == WS
     assert dec(ws=P, wsb=need - 1, part=7) == WS
-    n = pa.decode_num_workgroups(64, 16, 8, 4096)
+    n = pa.decode_num_workgroups(64, 16, 8, 128, 4096)
     assert 1 <= n <= 64 * 8 * 16
-    assert pa.decode_num_workgroups(1, 2, 1, 1) == 1
+    assert pa.decode_num_workgroups(1, 2, 1, 64, 1, torch.float32) == 1
+    assert pa.decode_num_workgroups(1, 2, 1, 96, 100) == 0
 
 
 def pre(**kw):
