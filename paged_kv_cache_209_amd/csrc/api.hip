@@ -234,7 +234,12 @@ pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const v
   a.num_kv_heads = num_kv_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
-  a.scale_log2 = scale * kLog2e;
+  // The kernel keeps scores in log2 units with a positive factor; a negative
+  // scale is applied by negating q, and a zero scale by a vanishing factor
+  // (every weight then rounds to exactly 1, the plain mean).
+  const float sl = scale * kLog2e;
+  a.scale_log2 = fabsf(sl) > 1e-30f ? fabsf(sl) : 1e-30f;
+  a.negate_q = sl < 0.0f ? 1 : 0;
   a.rows_per_tile = rows;
   a.num_workgroups = static_cast<int32_t>(max_units < cap ? max_units : cap);
   char* ws = static_cast<char*>(workspace);

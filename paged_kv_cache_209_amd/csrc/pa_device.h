@@ -104,6 +104,22 @@ __device__ __forceinline__ int add_agent(int* p, int v) {
 __device__ __forceinline__ void store_agent_int(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-byte agent-coherent accesses through a raw buffer descriptor (cache
+// policy sc1): the descriptor covers `bytes` bytes from `base` (out-of-range
+// offsets read 0 and drop writes).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kBufferFlags = 0x00020000;  // raw, untyped dword access
+constexpr int kPolicyAgent = 16;         // sc1: coherent at agent scope
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufferFlags);
+}
+__device__ __forceinline__ void store4_agent(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v), r, byte_off, 0, kPolicyAgent);
+}
+__device__ __forceinline__ f32x4_t load4_agent(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kPolicyAgent));
+}
+
 // Wait until every vector-memory operation this wave issued (stores included)
 // has completed: s_waitcnt vmcnt(0), leaving the other counters unconstrained.
 __device__ __forceinline__ void wait_vector_memory() {

@@ -63,7 +63,8 @@ struct PrefillArgs {
   int32_t num_kv_heads;
   int32_t max_blocks_per_seq;
   int32_t max_context_len;
-  float scale_log2;
+  float scale_log2;        // |scale * log2(e)|, at least 1e-30 (so that it is positive)
+  int32_t negate_q;        // 1 when the scale is negative: q is negated on load
   int32_t rows_per_tile;   // query rows per item: 128 (4 waves) or 32 (1 wave)
   int32_t num_workgroups;  // the key tiles of all items are split evenly over these
   int32_t* counters;       // [num_seqs * num_q_heads * (max_q_len + 1)], zero between calls

@@ -47,6 +47,7 @@ constexpr int kKeysPerTile = 64;
 constexpr int kRowsPerWave = 32;
 constexpr float kEmptyMaxP = -1.0e30f;
 constexpr float kSlack = 8.0f;
+constexpr int kNonTemporal = 2;  // cache-policy operand of direct-to-LDS loads: streaming
 
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
@@ -59,14 +60,19 @@ struct PShape {
   static constexpr int kTileBytes = kKeysPerTile * kRowBytes;
 };
 
-// LDS byte offset of 16-byte piece c of row r in a swizzled tile: piece c is
-// stored at slot c ^ (r mod pieces), so the 16 rows an MFMA operand read
-// touches fall on 16 different bank groups, with no padding bytes (which
-// direct-to-LDS loads could not skip).
+// Swizzled LDS tiles: 16-byte piece c of key row r is stored at slot
+// c ^ f(r) of that row (no padding bytes, which direct-to-LDS loads could not
+// skip). The K pattern spreads the 16 rows an MFMA operand read touches over
+// 16 bank groups; the V pattern spreads the 4 rows x 2 pieces of one
+// transpose-read lane group, and neighbouring lane groups, over distinct
+// bank groups.
 template <int D>
-__device__ __forceinline__ int swz(int r, int c) {
-  constexpr int P = PShape<D>::kPieces;
-  return r * PShape<D>::kRowBytes + ((c ^ (r & (P - 1))) << 4);
+__device__ __forceinline__ int k_swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  return D == 128 ? (((r & 3) << 1) | (((r >> 2) & 1) << 3)) : ((r & 3) << 1);
 }
 
 // s_waitcnt vmcnt(N): wait until at most N vector-memory operations of this
@@ -123,17 +129,104 @@ __device__ int units_per_head(const SeqGeom& s, int group) {
   return u;
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2), so workgroup ids w, w+8, w+16, ... share an L2. Give those workgroups
+// consecutive work ranges: the query tiles of one (sequence, KV head), which
+// stream the same K/V tiles, then run under one L2. A bijection on [0, G).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_local_range(int wg, int G) {
+  const int per = G / kXcds;
+  if (wg >= per * kXcds) return wg;  // the remainder keeps its own id
+  return (wg % kXcds) * per + wg / kXcds;
+}
+
 __device__ __forceinline__ int owner_of_unit(int64_t u, int64_t U, int64_t G) {
   return static_cast<int>(((u + 1) * G - 1) / U);
 }
 
+// Where the rows of a key tile come from: the pool (through the block table)
+// for positions below c, the call's k/v for the new tokens.
+template <int D, int NT>
+struct TileSrc {
+  const bf16_t* kpool;
+  const bf16_t* vpool;
+  const bf16_t* kg;
+  const bf16_t* vg;
+  const int32_t* table;
+  int64_t tok_stride;
+  int64_t head_off;
+  int start;  // first row of the sequence's new tokens in k/v
+  int c;      // cached positions
+  int total;  // cached + new positions
+};
+
+// Issue the direct-to-LDS loads of key tile kt into one stage ([K tile | V
+// tile]). Each wave instruction fills 1 KB of LDS in lane order. A tile that
+// lies wholly in the pool or wholly in the new tokens uses one wave-uniform
+// base plus the precomputed lane offsets; a tile that straddles the two, or
+// runs past the last key (its rows re-read the last key), resolves each
+// lane's row on its own.
+template <int D, int NT>
+__device__ __forceinline__ void issue_tile(const TileSrc<D, NT>& t, int kt, char* stage,
+                                           const int (&krow)[kKeysPerTile * PShape<D>::kPieces / NT],
+                                           const int (&kgo)[kKeysPerTile * PShape<D>::kPieces / NT],
+                                           const int (&vgo)[kKeysPerTile * PShape<D>::kPieces / NT], int tid,
+                                           int wave) {
+  constexpr int kIters = kKeysPerTile * PShape<D>::kPieces / NT;
+  constexpr int TB = PShape<D>::kTileBytes;
+  const int k0 = kt * kKeysPerTile;
+  char* kdst = stage;
+  char* vdst = stage + TB;
+  const bool in_pool = k0 + kKeysPerTile <= t.c;
+  const bool in_new = k0 >= t.c && k0 + kKeysPerTile <= t.total;
+  if (in_pool || in_new) {
+    int64_t row0;
+    const bf16_t* kb;
+    const bf16_t* vb;
+    if (in_pool) {
+      const int block = __builtin_amdgcn_readfirstlane(t.table[k0 / kTokensPerBlock]);
+      row0 = static_cast<int64_t>(block) * kTokensPerBlock + k0 % kTokensPerBlock;
+      kb = t.kpool;
+      vb = t.vpool;
+    } else {
+      row0 = static_cast<int64_t>(t.start) + (k0 - t.c);
+      kb = t.kg;
+      vb = t.vg;
+    }
+    kb += row0 * t.tok_stride + t.head_off;
+    vb += row0 * t.tok_stride + t.head_off;
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int lds_off = (it * NT + wave * kWave) * 16;
+      __builtin_amdgcn_global_load_lds(kb + kgo[it], (lds_void_t*)(kdst + lds_off), 16, 0, kNonTemporal);
+      __builtin_amdgcn_global_load_lds(vb + vgo[it], (lds_void_t*)(vdst + lds_off), 16, 0, kNonTemporal);
+    }
+  } else {
+    const int block = k0 < t.c ? __builtin_amdgcn_readfirstlane(t.table[k0 / kTokensPerBlock]) : 0;
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int kr = krow[it];
+      const int lds_off = (it * NT + wave * kWave) * 16;
+      const int pos = min(k0 + kr, t.total - 1);
+      const bool cached = pos < t.c;
+      const int64_t row = cached ? static_cast<int64_t>(block) * kTokensPerBlock + pos % kTokensPerBlock
+                                 : static_cast<int64_t>(t.start) + (pos - t.c);
+      // kgo/vgo hold kr * tok_stride + piece; re-base them on the lane's own row
+      const int64_t base = (row - kr) * t.tok_stride + t.head_off;
+      const bf16_t* ksrc = (cached ? t.kpool : t.kg) + base + kgo[it];
+      const bf16_t* vsrc = (cached ? t.vpool : t.vg) + base + vgo[it];
+      __builtin_amdgcn_global_load_lds(ksrc, (lds_void_t*)(kdst + lds_off), 16, 0, kNonTemporal);
+      __builtin_amdgcn_global_load_lds(vsrc, (lds_void_t*)(vdst + lds_off), 16, 0, kNonTemporal);
+    }
+  }
+}
+
 template <int D, int WM>
-__global__ __launch_bounds__(64 * WM) void paged_prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a) {
   using S = PShape<D>;
   constexpr int ROWS = kRowsPerWave * WM;
   constexpr int NT = kWave * WM;
   constexpr int TB = S::kTileBytes;
-  constexpr int kLoadsPerTile = 2 * kKeysPerTile * S::kPieces / NT;  // per thread, K and V
   // Two stages of [K tile | V tile]: tile t+1 streams in while t is used.
   __shared__ __attribute__((aligned(16))) char s_kv[2][2 * TB];
   __shared__ int s_scan[NT];
@@ -169,7 +262,7 @@ __global__ __launch_bounds__(64 * WM) void paged_prefill_kernel(PrefillArgs a) {
   const int64_t U = __builtin_amdgcn_readfirstlane(s_scan[NT - 1]);
   if (U == 0) return;
   const int64_t G = min(static_cast<int64_t>(gridDim.x), U);
-  const int w = blockIdx.x;
+  const int w = xcd_local_range(static_cast<int>(blockIdx.x), static_cast<int>(G));
   if (w >= G) return;
   const int64_t u_begin = static_cast<int64_t>(w) * U / G;
   const int64_t u_end = static_cast<int64_t>(w + 1) * U / G;
@@ -197,14 +290,48 @@ __global__ __launch_bounds__(64 * WM) void paged_prefill_kernel(PrefillArgs a) {
   int seq = __builtin_amdgcn_readfirstlane(s_loc[0]);
   int64_t seq_base = __builtin_amdgcn_readfirstlane(s_loc[1]);
 
+  // Per-lane LDS offsets of the MFMA operands, fixed for the whole kernel:
+  // K rows 16mt + col, piece 4kc + grp (the mt step is an immediate);
+  // V transpose reads rows 32kc2 + 4grp + col/4 (+16), 4 dims at
+  // 16dt + 4(col%4) (the kc2 and +16 steps are immediates).
+  constexpr int RB = S::kRowBytes;
+  int koff[S::kDChunks];
+#pragma unroll
+  for (int kc = 0; kc < S::kDChunks; ++kc) koff[kc] = col * RB + (((kc * 4 + grp) ^ k_swz<D>(col)) << 4);
+  int voff[S::kDTiles];
+  {
+    const int vr = grp * 4 + (col >> 2);
+#pragma unroll
+    for (int dt = 0; dt < S::kDTiles; ++dt)
+      voff[dt] = vr * RB + (((dt * 2 + ((col & 3) >> 1)) ^ v_swz<D>(vr)) << 4) + (col & 1) * 8;
+  }
+  // Per-lane global element offsets of the tile loads (row kr of the tile,
+  // the 16-byte piece that lands in this lane's LDS slot), for K and V.
+  constexpr int kIters = kKeysPerTile * S::kPieces / NT;
+  const int64_t tok_stride = static_cast<int64_t>(Hkv) * D;  // elements between token rows
+  int krow[kIters], kgo[kIters], vgo[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int idx = it * NT + tid;
+    const int kr = idx / S::kPieces;
+    const int slot = idx % S::kPieces;
+    krow[it] = kr;
+    kgo[it] = kr * static_cast<int>(tok_stride) + ((slot ^ k_swz<D>(kr)) << 3);
+    vgo[it] = kr * static_cast<int>(tok_stride) + ((slot ^ v_swz<D>(kr)) << 3);
+  }
+
   const bf16_t* qg = static_cast<const bf16_t*>(a.q);
   const bf16_t* kg = static_cast<const bf16_t*>(a.k);
   const bf16_t* vg = static_cast<const bf16_t*>(a.v);
   const bf16_t* kpool = static_cast<const bf16_t*>(a.k_cache);
   const bf16_t* vpool = static_cast<const bf16_t*>(a.v_cache);
   bf16_t* outp = static_cast<bf16_t*>(a.out);
-  const int64_t tok_stride = static_cast<int64_t>(Hkv) * D;  // elements between token rows (k, v, pools)
+  // Scores are kept in log2 units: p = 2^(s*sc - m). The host passes
+  // sc = |scale * log2(e)| (never 0) and asks for q to be negated when the
+  // scale is negative, so that max(s) * sc is the scaled maximum.
   const float sc = a.scale_log2;
+  const uint32_t qflip = a.negate_q ? 0x80008000u : 0u;
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
   // ---- 3. Segments.
   int64_t u = u_begin;
@@ -244,7 +371,9 @@ __global__ __launch_bounds__(64 * WM) void paged_prefill_kernel(PrefillArgs a) {
       const bf16_t* qrow = qg + (static_cast<int64_t>(sg.start + jj) * a.num_q_heads + h * group + g) * D;
 #pragma unroll
       for (int kc = 0; kc < S::kDChunks; ++kc) {
-        qf[nt][kc] = *reinterpret_cast<const bf16x8_t*>(qrow + kc * 32 + grp * 8);
+        u32x4_t w4 = *reinterpret_cast<const u32x4_t*>(qrow + kc * 32 + grp * 8);
+        w4 ^= qflip;
+        qf[nt][kc] = __builtin_bit_cast(bf16x8_t, w4);
       }
     }
     // Keys a query column may see: positions <= c + j, clamped to the last key.
@@ -256,51 +385,36 @@ __global__ __launch_bounds__(64 * WM) void paged_prefill_kernel(PrefillArgs a) {
     const int wave_min_vis = min(sg.c + (qt * ROWS + wave * kRowsPerWave) / group, total_keys - 1);
 
     f32x4_t acc_o[2][S::kDTiles];
-    float m[2], l[2];
+    f32x4_t lsum[2];  // row sums from an MFMA with a ones operand (all 4 entries equal)
+    float m[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       m[nt] = kEmptyMaxP;
-      l[nt] = 0.0f;
+      lsum[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int dt = 0; dt < S::kDTiles; ++dt) acc_o[nt][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
     const int32_t* table = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks_per_seq;
-    // Issue the direct-to-LDS loads of key tile kt into stage `stage`. Each
-    // wave instruction fills 1 KB of LDS in lane order; lane slot (row, slot)
-    // fetches global piece slot ^ (row mod pieces) of that row, which is
-    // exactly the swizzled layout. Rows past the last key re-read it.
-    auto issue_tile = [&](int kt, int stage) {
-      const int k0 = kt * kKeysPerTile;
-      const int block = k0 < sg.c ? table[k0 / kTokensPerBlock] : 0;
-      char* kdst = s_kv[stage];
-      char* vdst = s_kv[stage] + TB;
-#pragma unroll
-      for (int it = 0; it < kKeysPerTile * S::kPieces / NT; ++it) {
-        const int idx = it * NT + tid;
-        const int kr = idx / S::kPieces;
-        const int slot = idx % S::kPieces;
-        const int pc = slot ^ (kr & (S::kPieces - 1));
-        const int pos = min(k0 + kr, total_keys - 1);
-        const bool cached = pos < sg.c;
-        const int64_t row = cached ? static_cast<int64_t>(block) * kTokensPerBlock + pos % kTokensPerBlock
-                                   : static_cast<int64_t>(sg.start) + (pos - sg.c);
-        const int64_t off = row * tok_stride + h * D + pc * 8;
-        const bf16_t* ksrc = (cached ? kpool : kg) + off;
-        const bf16_t* vsrc = (cached ? vpool : vg) + off;
-        const int lds_off = (it * NT + wave * kWave) * 16;  // this wave instruction's 1 KB
-        __builtin_amdgcn_global_load_lds(ksrc, (lds_void_t*)(kdst + lds_off), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vsrc, (lds_void_t*)(vdst + lds_off), 16, 0, 0);
-      }
-    };
-
-    if (t_lo < t_hi) issue_tile(t_lo, 0);
+    const int64_t head_off = static_cast<int64_t>(h) * D;
+    TileSrc<D, NT> src;
+    src.kpool = kpool;
+    src.vpool = vpool;
+    src.kg = kg;
+    src.vg = vg;
+    src.table = table;
+    src.tok_stride = tok_stride;
+    src.head_off = head_off;
+    src.start = sg.start;
+    src.c = sg.c;
+    src.total = total_keys;
+    if (t_lo < t_hi) issue_tile<D, NT>(src, t_lo, s_kv[0], krow, kgo, vgo, tid, wave);
     for (int kt = t_lo; kt < t_hi; ++kt) {
       const int k0 = kt * kKeysPerTile;
       const int stage = (kt - t_lo) & 1;
       if (kt + 1 < t_hi) {
-        issue_tile(kt + 1, stage ^ 1);
-        wait_vmcnt<kLoadsPerTile>();  // this tile's loads are done, the next one's may fly
+        issue_tile<D, NT>(src, kt + 1, s_kv[stage ^ 1], krow, kgo, vgo, tid, wave);
+        wait_vmcnt<2 * kIters>();  // this tile's loads are done, the next one's may fly
       } else {
         wait_vmcnt<0>();
       }
@@ -316,98 +430,88 @@ __global__ __launch_bounds__(64 * WM) void paged_prefill_kernel(PrefillArgs a) {
         st[mt][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kc = 0; kc < S::kDChunks; ++kc) {
-          const bf16x8_t kfrag = *reinterpret_cast<const bf16x8_t*>(s_k + swz<D>(mt * 16 + col, kc * 4 + grp));
+          const bf16x8_t kfrag = *reinterpret_cast<const bf16x8_t*>(s_k + koff[kc] + mt * 16 * RB);
           st[mt][0] = mfma16(kfrag, qf[0][kc], st[mt][0]);
           st[mt][1] = mfma16(kfrag, qf[1][kc], st[mt][1]);
         }
       }
 
-      // -- online softmax per query column
+      // -- online softmax per query column (raw scores; sc > 0)
       const bool full_tile = k0 + kKeysPerTile - 1 <= wave_min_vis;
-      uint32_t pw[2][2][4];  // [nt][kc2][word]: P^T operand, bf16 pairs
+      if (!full_tile) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (k0 + mt * 16 + grp * 4 + e > vis[nt]) st[mt][nt][e] = -INFINITY;
+      }
       bool need = false;
       float mx[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        float tmax = -INFINITY;
+        float t = fmaxf(fmaxf(st[0][nt][0], st[0][nt][1]), fmaxf(st[0][nt][2], st[0][nt][3]));
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float s = st[mt][nt][e] * sc;
-            if (!full_tile) {
-              const int kp = k0 + mt * 16 + grp * 4 + e;
-              s = kp <= vis[nt] ? s : -INFINITY;
-            }
-            st[mt][nt][e] = s;
-            tmax = fmaxf(tmax, s);
-          }
-        }
-        tmax = fmaxf(tmax, shfl_xor_f32(tmax, 16));
-        tmax = fmaxf(tmax, shfl_xor_f32(tmax, 32));
-        mx[nt] = fmaxf(m[nt], tmax);
+        for (int mt = 1; mt < 4; ++mt)
+          t = fmaxf(t, fmaxf(fmaxf(st[mt][nt][0], st[mt][nt][1]), fmaxf(st[mt][nt][2], st[mt][nt][3])));
+        t = fmaxf(t, shfl_xor_f32(t, 16));
+        t = fmaxf(t, shfl_xor_f32(t, 32));
+        mx[nt] = fmaxf(m[nt], t * sc);
         need |= mx[nt] > m[nt] + kSlack;
       }
       if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const float alpha = exp2_fast(m[nt] - mx[nt]);
-          l[nt] *= alpha;
+          lsum[nt] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < S::kDTiles; ++dt) acc_o[nt][dt] *= alpha;
           m[nt] = mx[nt];
         }
       }
+      // P^T operands, bf16: for key step kc2 the lane's 8 keys are
+      // {4grp..4grp+3} of S^T tile 2kc2 and the same of tile 2kc2+1.
+      bf16x8_t pb[2][2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
+        const float nm = -m[nt];
 #pragma unroll
         for (int kc2 = 0; kc2 < 2; ++kc2) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const f32x4_t& sv = st[2 * kc2 + half][nt];
-            const uint32_t w0 = pack_bf16x2(exp2_fast(sv[0] - m[nt]), exp2_fast(sv[1] - m[nt]));
-            const uint32_t w1 = pack_bf16x2(exp2_fast(sv[2] - m[nt]), exp2_fast(sv[3] - m[nt]));
-            pw[nt][kc2][2 * half + 0] = w0;
-            pw[nt][kc2][2 * half + 1] = w1;
-            l[nt] += (bf16_lo(w0) + bf16_hi(w0)) + (bf16_lo(w1) + bf16_hi(w1));
-          }
+          const f32x4_t& s0 = st[2 * kc2][nt];
+          const f32x4_t& s1 = st[2 * kc2 + 1][nt];
+          const u32x4_t w = {pack_bf16x2(exp2_fast(fmaf(s0[0], sc, nm)), exp2_fast(fmaf(s0[1], sc, nm))),
+                             pack_bf16x2(exp2_fast(fmaf(s0[2], sc, nm)), exp2_fast(fmaf(s0[3], sc, nm))),
+                             pack_bf16x2(exp2_fast(fmaf(s1[0], sc, nm)), exp2_fast(fmaf(s1[1], sc, nm))),
+                             pack_bf16x2(exp2_fast(fmaf(s1[2], sc, nm)), exp2_fast(fmaf(s1[3], sc, nm)))};
+          pb[nt][kc2] = __builtin_bit_cast(bf16x8_t, w);
         }
       }
 
-      // -- O^T += V^T P^T
+      // -- O^T += V^T P^T, and the row sums from the same bf16 P
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2) {
-        const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0][kc2][0], pw[0][kc2][1], pw[0][kc2][2], pw[0][kc2][3]});
-        const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[1][kc2][0], pw[1][kc2][1], pw[1][kc2][2], pw[1][kc2][3]});
-        const int key_a = kc2 * 32 + grp * 4 + (col >> 2);
-        const int key_b = key_a + 16;
-        const int half = (col & 1) * 8;  // byte offset of the lane's 4 dims inside a 16-byte piece
 #pragma unroll
         for (int dt = 0; dt < S::kDTiles; ++dt) {
-          const int pc = dt * 2 + ((col & 3) >> 1);
-          const i16x4_t ta =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(s_v + swz<D>(key_a, pc) + half));
-          const i16x4_t tb =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(s_v + swz<D>(key_b, pc) + half));
+          const char* pv = s_v + voff[dt] + kc2 * 32 * RB;
+          const i16x4_t ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(pv));
+          const i16x4_t tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(pv + 16 * RB));
           typedef short i16x8_t __attribute__((ext_vector_type(8)));
           const i16x8_t t8 = {ta[0], ta[1], ta[2], ta[3], tb[0], tb[1], tb[2], tb[3]};
           const bf16x8_t vfrag = __builtin_bit_cast(bf16x8_t, t8);
-          acc_o[0][dt] = mfma16(vfrag, pb0, acc_o[0][dt]);
-          acc_o[1][dt] = mfma16(vfrag, pb1, acc_o[1][dt]);
+          acc_o[0][dt] = mfma16(vfrag, pb[0][kc2], acc_o[0][dt]);
+          acc_o[1][dt] = mfma16(vfrag, pb[1][kc2], acc_o[1][dt]);
         }
+        lsum[0] = mfma16(ones, pb[0][kc2], lsum[0]);
+        lsum[1] = mfma16(ones, pb[1][kc2], lsum[1]);
       }
       __syncthreads();  // the next tile overwrites the LDS tiles
     }
 
-    // ---- finish the segment: lane group sums of l, then output or partial
+    // ---- finish the segment: output or partial
     float lt[2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float x = l[nt];
-      x += shfl_xor_f32(x, 16);
-      x += shfl_xor_f32(x, 32);
-      lt[nt] = x;
-    }
+    for (int nt = 0; nt < 2; ++nt) lt[nt] = lsum[nt][0];
     const int first_owner = owner_of_unit(item_first, U, G);
     const int n_parts = owner_of_unit(item_end - 1, U, G) - first_owner + 1;
     if (n_parts == 1) {
@@ -431,17 +535,15 @@ __global__ __launch_bounds__(64 * WM) void paged_prefill_kernel(PrefillArgs a) {
       // merge gives it weight 0.
       const int which = u > u_begin ? 1 : 0;
       const int64_t slot = 2 * static_cast<int64_t>(w) + which;
+      const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(a.part_out + slot * ROWS * D, ROWS * D * 4);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int row = wave * kRowsPerWave + nt * 16 + col;
         const bool seen = lt[nt] > 0.0f;
         const float inv = seen ? 1.0f / lt[nt] : 0.0f;
-        float* po = a.part_out + (slot * ROWS + row) * D;
 #pragma unroll
-        for (int dt = 0; dt < S::kDTiles; ++dt) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) store_agent(po + dt * 16 + grp * 4 + e, acc_o[nt][dt][e] * inv);
-        }
+        for (int dt = 0; dt < S::kDTiles; ++dt)
+          store4_agent(pr, (row * D + dt * 16 + grp * 4) * 4, acc_o[nt][dt] * inv);
         if (grp == 0) store_agent(a.part_lse + slot * ROWS + row, seen ? m[nt] + __log2f(lt[nt]) : -INFINITY);
       }
       wait_vector_memory();
@@ -487,13 +589,13 @@ __global__ __launch_bounds__(64 * WM) void paged_prefill_kernel(PrefillArgs a) {
           }
           for (int p = 0; p < n_parts; ++p) {
             const int64_t sl = 2 * static_cast<int64_t>(first_owner + p) + ((p == 0 && first_start < item_first) ? 1 : 0);
+            const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(a.part_out + sl * ROWS * D, ROWS * D * 4);
 #pragma unroll
             for (int k = 0; k < kMergeRows; ++k) {
               const int row = rb + k * kRowStep;
               if (row >= ROWS) continue;
               const float f = exp2_fast(load_agent(a.part_lse + sl * ROWS + row) - mxr[k]);
-              const float* po = a.part_out + (sl * ROWS + row) * D + 4 * d4;
-              const f32x4_t o4 = {load_agent(po), load_agent(po + 1), load_agent(po + 2), load_agent(po + 3)};
+              const f32x4_t o4 = load4_agent(pr, (row * D + 4 * d4) * 4);
               num[k] += f * o4;
               den[k] += f;
             }
