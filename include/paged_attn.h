@@ -47,7 +47,10 @@
  *   streams) must not share a workspace.
  * Workspaces. Decode and prefill lay out their scratch differently: a
  *   workspace zero-filled once may be reused by any number of calls of ONE
- *   of the two entry points, never by both.
+ *   of the two entry points, whatever their sizes, never by both. (Partial
+ *   results sit in fixed-size regions at the start; the counters follow at
+ *   an offset that does not depend on the call's sizes, and every completed
+ *   call leaves them zero.)
  */
 #ifndef PAGED_ATTN_H_
 #define PAGED_ATTN_H_
@@ -122,7 +125,7 @@ pa_status pa_kv_store(void* k_cache, void* v_cache, const void* k, const void* v
  *                must see it zero-filled (e.g. from a zeroing allocation);
  *                every completed call leaves its counter words zero again, so
  *                the same workspace can be reused without clearing.
- *                workspace may be NULL when max_context_len <= block_size
+ *                workspace may be NULL when max_context_len <= 64
  *                (pa_decode_workspace_bytes returns 0 then).
  * Supported dtypes: PA_F32, PA_BF16.
  */
@@ -136,12 +139,13 @@ pa_status pa_paged_attn_decode(void* out, const void* q, const void* k_cache, co
 
 /*
  * pa_paged_attn_decode_ex -- pa_paged_attn_decode with an explicit number of
- * workgroups (0 = the library's choice, the same as pa_paged_attn_decode).
- * The decode work -- every 256-token block of every (sequence, query-head
- * group) -- is cut into num_workgroups equal contiguous shares, so a long
- * context may be split over several workgroups and merged afterwards.
- * Results for one num_workgroups value are bit-identical from run to run;
- * different values agree to rounding.
+ * workgroups, 0 to 2048 (0 = the library's choice, the same as
+ * pa_paged_attn_decode; more than 2048 is PA_ERR_INVALID_ARG). The decode
+ * work -- every 64 tokens of every (sequence, query-head group) -- is cut
+ * into num_workgroups equal contiguous shares, so a long context may be split
+ * over several workgroups and merged afterwards. Results for one
+ * num_workgroups value are bit-identical from run to run; different values
+ * agree to rounding.
  */
 pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* block_tables, const int32_t* context_lens,
@@ -153,18 +157,20 @@ pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache,
 
 /*
  * Number of workgroups pa_paged_attn_decode launches for these sizes on the
- * current device: as many as are resident at once (occupancy per compute unit
- * times compute units), capped by the number of work units. 0 for sizes the
- * library does not support. Queries the HIP runtime (falls back to 256 compute
- * units when no device is visible).
+ * current device: two per compute unit when the kernel's occupancy allows it
+ * (else as many as are resident at once), capped by the number of work units
+ * and by 2048. 0 for sizes the library does not support. Queries the HIP
+ * runtime (falls back to 256 compute units when no device is visible).
  */
 int32_t pa_decode_num_workgroups(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len, pa_dtype dtype);
 
 /*
  * Workspace bytes that decode needs for these sizes with any number of
- * workgroups (an upper bound; 0 when max_context_len fits in one block).
- * max_q_len is ignored (decode has one query token per sequence).
+ * workgroups: one counter per (sequence, query head) plus two partial-result
+ * slots per workgroup of the largest grid, so it does not grow with the
+ * context length (0 when max_context_len <= 64, where nothing is ever
+ * split). max_q_len is ignored (decode has one query token per sequence).
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_q_len, int32_t max_context_len);

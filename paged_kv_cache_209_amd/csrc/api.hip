@@ -30,28 +30,24 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 pa_status to_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-// Upper bound of decode work units: one per 256-token block of the longest
+// Upper bound of decode work units: one per 64 tokens of the longest
 // context, for every (sequence, query-head group).
 int64_t decode_max_units(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len) {
   const int64_t head_groups = num_q_heads / pa::decode_head_group(num_q_heads / num_kv_heads);
-  return static_cast<int64_t>(num_seqs) * head_groups * ceil_div(max_context_len, kBlockSize);
+  return static_cast<int64_t>(num_seqs) * head_groups * ceil_div(max_context_len, pa::kDecodeUnitTokens);
 }
 
+// An item is split over workgroups only if its context has more than one unit.
 size_t decode_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= kBlockSize) return 0;
-  const int64_t max_parts = ceil_div(max_context_len, kBlockSize);
-  return pa::workspace_layout(num_seqs, num_q_heads, head_dim, 1, max_parts).total();
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= pa::kDecodeUnitTokens) return 0;
+  return pa::decode_workspace_layout(num_seqs, num_q_heads).total;
 }
 
 // Prefill workspace: one counter per (sequence, query head, query tile) bound
 // and two partial-result pieces per workgroup of the largest grid.
-pa::WorkspaceLayout prefill_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_q_len) {
-  pa::WorkspaceLayout w;
+pa::WorkspaceLayout prefill_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_q_len) {
   const int64_t counters = static_cast<int64_t>(num_seqs) * num_q_heads * (static_cast<int64_t>(max_q_len) + 1);
-  w.counters_bytes = static_cast<size_t>((counters * 4 + 255) / 256 * 256);
-  w.lse_bytes = static_cast<size_t>((pa::kPrefillSlotRows * 4 + 255) / 256 * 256);
-  w.out_bytes = static_cast<size_t>(pa::kPrefillSlotRows * head_dim * 4);
-  return w;
+  return pa::make_workspace_layout(pa::kPrefillSlotRows, counters);
 }
 
 }  // namespace
@@ -124,19 +120,18 @@ pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache,
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
     return PA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
-  if (num_workgroups < 0) return PA_ERR_INVALID_ARG;
+  if (num_workgroups < 0 || num_workgroups > pa::kDecodeMaxWorkgroups) return PA_ERR_INVALID_ARG;
   if (k_cache == nullptr || v_cache == nullptr) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0) return PA_OK;
   if (out == nullptr || q == nullptr || block_tables == nullptr || context_lens == nullptr) return PA_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID_ARG;
 
-  const int64_t max_parts = ceil_div(max_context_len, kBlockSize);
-  pa::WorkspaceLayout lay = pa::workspace_layout(num_seqs, num_q_heads, head_dim, 1, max_parts);
+  const pa::WorkspaceLayout lay = pa::decode_workspace_layout(num_seqs, num_q_heads);
   // An item is split over workgroups only if some workgroup gets less than a
-  // whole item; with one block per context nothing is ever split.
-  const bool split = max_parts > 1 && num_workgroups != 1;
+  // whole item; with one unit per context nothing is ever split.
+  const bool split = max_context_len > pa::kDecodeUnitTokens && num_workgroups != 1;
   if (split) {
-    if (workspace == nullptr || workspace_bytes < lay.total()) return PA_ERR_WORKSPACE;
+    if (workspace == nullptr || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
   }
 
@@ -154,12 +149,11 @@ pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache,
   a.max_context_len = max_context_len;
   a.num_workgroups = num_workgroups;  // 0: one resident round, chosen by the launcher
   a.max_units = decode_max_units(num_seqs, num_q_heads, num_kv_heads, max_context_len);
-  a.max_parts = static_cast<int32_t>(max_parts);
   a.scale_log2 = scale * kLog2e;
   char* ws = static_cast<char*>(workspace);
-  a.counters = split ? reinterpret_cast<int32_t*>(ws) : nullptr;
-  a.part_lse = split ? reinterpret_cast<float*>(ws + lay.counters_bytes) : nullptr;
-  a.part_out = split ? reinterpret_cast<float*>(ws + lay.counters_bytes + lay.lse_bytes) : nullptr;
+  a.counters = split ? reinterpret_cast<int32_t*>(ws + lay.counters_off) : nullptr;
+  a.part_lse = split ? reinterpret_cast<float*>(ws + lay.lse_off) : nullptr;
+  a.part_out = split ? reinterpret_cast<float*>(ws + lay.out_off) : nullptr;
   (void)hipGetLastError();
   return to_status(pa::launch_decode(a, dtype == PA_BF16 ? pa::Dtype::kBF16 : pa::Dtype::kF32, head_dim,
                                      static_cast<hipStream_t>(stream)));
@@ -179,7 +173,7 @@ pa_status pa_paged_attn_decode(void* out, const void* q, const void* k_cache, co
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_q_len,
                                   int32_t max_context_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_q_len <= 0 || max_context_len <= 0) return 0;
-  return prefill_layout(num_seqs, num_q_heads, head_dim, max_q_len).total();
+  return prefill_layout(num_seqs, num_q_heads, max_q_len).total;
 }
 
 pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const void* v, const void* k_cache,
@@ -207,8 +201,8 @@ pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const v
   if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_cache) ||
       !aligned16(v_cache))
     return PA_ERR_INVALID_ARG;
-  const pa::WorkspaceLayout lay = prefill_layout(num_seqs, num_q_heads, head_dim, max_q_len);
-  if (workspace == nullptr || workspace_bytes < lay.total()) return PA_ERR_WORKSPACE;
+  const pa::WorkspaceLayout lay = prefill_layout(num_seqs, num_q_heads, max_q_len);
+  if (workspace == nullptr || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
 
   const int32_t group = num_q_heads / num_kv_heads;
@@ -243,9 +237,9 @@ pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const v
   a.rows_per_tile = rows;
   a.num_workgroups = static_cast<int32_t>(max_units < cap ? max_units : cap);
   char* ws = static_cast<char*>(workspace);
-  a.counters = reinterpret_cast<int32_t*>(ws);
-  a.part_lse = reinterpret_cast<float*>(ws + lay.counters_bytes);
-  a.part_out = reinterpret_cast<float*>(ws + lay.counters_bytes + lay.lse_bytes);
+  a.counters = reinterpret_cast<int32_t*>(ws + lay.counters_off);
+  a.part_lse = reinterpret_cast<float*>(ws + lay.lse_off);
+  a.part_out = reinterpret_cast<float*>(ws + lay.out_off);
   (void)hipGetLastError();
   return to_status(pa::launch_prefill(a, head_dim, static_cast<hipStream_t>(stream)));
 }

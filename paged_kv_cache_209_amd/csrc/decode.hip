@@ -30,11 +30,13 @@
 //   * at the end of a segment the 8 groups of a wave merge by lane shuffles,
 //     the 4 waves through LDS; a whole item is written as the final output,
 //     a piece as a (normalised output, log2-sum-exp) partial.
-//   * The last workgroup to finish a piece of a split item -- found with a
-//     device-scope counter -- merges all its pieces in order. The merge order
-//     is fixed, so results are bit-identical from run to run; no floating-
-//     point atomics are used. Partials move through agent-coherent atomic
-//     stores/loads, never through cache-wide fences.
+//   * consecutive segments overlap: the next segment's block-table window,
+//     query rows and first chunk load while the current one finishes;
+//   * the pieces of a split item are counted on a device-scope counter per
+//     item, one count per wave and piece, when the workgroup ends; the wave
+//     whose count completes the item merges all its pieces, in piece order,
+//     so results are bit-identical from run to run and no floating-point
+//     atomics are used.
 #include <math.h>
 
 #include "pa_device.h"
@@ -180,25 +182,47 @@ struct BlockWindow {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
+  // Starts loading the window at b without waiting: for a segment that
+  // follows the current one, whose ids are first needed a whole segment later.
+  __device__ __forceinline__ void fill_async(int b, int lane) {
+    base = b;
+    id = b + lane < limit ? table[b + lane] : 0;
+  }
   __device__ __forceinline__ int get(int b, int lane) {
     if (b - base >= kWave) fill(b - (b - base) % kWave, lane);  // wave-uniform, rare
     return __builtin_amdgcn_readlane(id, b - base);
   }
 };
 
+// The lane's words of query head g, read from the wave's copy of the group's
+// query rows in LDS (the same pieces of the row that the lane loads of K).
+template <typename T, int D>
+__device__ __forceinline__ void q_words(const u32x4_t* sq, int g, int sl, uint32_t (&w)[DecodeShape<T, D>::kWords]) {
+  using S = DecodeShape<T, D>;
+#pragma unroll
+  for (int v = 0; v < S::kVecs; ++v) {
+    const u32x4_t x = sq[(g * D + v * S::kVecStride + sl * S::kElemsPerVec) * Elem<T>::kBytes / 16];
+    w[4 * v + 0] = x[0];
+    w[4 * v + 1] = x[1];
+    w[4 * v + 2] = x[2];
+    w[4 * v + 3] = x[3];
+  }
+}
+
 template <typename T, int D, int GT>
 __device__ __forceinline__ void consume_chunk(LaneState<GT, DecodeShape<T, D>::kLaneElems>& st,
-                                              const Chunk<DecodeShape<T, D>::kWords>& c,
-                                              const uint32_t (&qw)[GT][DecodeShape<T, D>::kWords], bool va, bool vb,
-                                              float sc) {
+                                              const Chunk<DecodeShape<T, D>::kWords>& c, const u32x4_t* sq, int sl,
+                                              bool va, bool vb, float sc) {
   constexpr int W = DecodeShape<T, D>::kWords;
   constexpr int E = DecodeShape<T, D>::kLaneElems;
   float sa[GT], sb[GT];
   bool need = false;
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
-    const float da = sum8(partial_dot<T, D>(qw[g], c.ka));
-    const float db = sum8(partial_dot<T, D>(qw[g], c.kb));
+    uint32_t qw[W];
+    q_words<T, D>(sq, g, sl, qw);
+    const float da = sum8(partial_dot<T, D>(qw, c.ka));
+    const float db = sum8(partial_dot<T, D>(qw, c.kb));
     sa[g] = va ? da * sc : -INFINITY;
     sb[g] = vb ? db * sc : -INFINITY;
     need |= fmaxf(sa[g], sb[g]) > st.m[g] + kStaleMaxSlack;
@@ -241,37 +265,161 @@ __device__ __forceinline__ void consume_chunk(LaneState<GT, DecodeShape<T, D>::k
   }
 }
 
-// Blocks of a context, with the length clamped to [0, max_context_len]
-// (lengths outside [1, max_context_len] are a caller error; clamping keeps
-// every read inside the block table and the workspace, and every loop finite).
-__device__ __forceinline__ int context_blocks(int ctx, int max_ctx) {
+// Work units (64 tokens each) of a context, with the length clamped to
+// [0, max_context_len] (lengths outside [1, max_context_len] are a caller
+// error; clamping keeps every read inside the block table and every loop
+// finite).
+__device__ __forceinline__ int context_units(int ctx, int max_ctx) {
   ctx = min(max(ctx, 0), max_ctx);
-  return (ctx + kTokensPerBlock - 1) / kTokensPerBlock;
+  return (ctx + kDecodeUnitTokens - 1) / kDecodeUnitTokens;
 }
 
-// Which workgroup owns work unit u when U units are split evenly over G
-// workgroups (workgroup w owns [w*U/G, (w+1)*U/G)).
-__device__ __forceinline__ int owner_of(int64_t u, int64_t U, int64_t G) {
-  return static_cast<int>(((u + 1) * G - 1) / U);
+// The U work units are split into G equal contiguous ranges, one per
+// workgroup: workgroup w owns [start(w), start(w + 1)). With G <= U every
+// range is non-empty, so the owners of an item's units are consecutive
+// workgroups.
+struct EvenSplit {
+  int64_t U, G;
+  __device__ __forceinline__ int64_t start(int64_t w) const { return U * w / G; }
+  __device__ __forceinline__ int64_t owner(int64_t u) const { return ((u + 1) * G - 1) / U; }
+};
+
+// The piece of one item (sequence, head group) that lies in a workgroup's
+// unit range: the tokens it covers and the blocks that hold them.
+struct Segment {
+  int seq, hg;
+  int t_lo, t_hi;       // tokens [t_lo, t_hi)
+  int b_lo, b_hi;       // blocks [b_lo, b_hi) holding them
+  int n_parts;          // pieces of the item over all workgroups
+  int64_t first_owner;  // workgroup holding the item's first piece
+  int64_t item_end;     // one past the item's last unit
+};
+
+// Walks the segments of the unit range [u, u_end) in order. All its state is
+// wave-uniform (kept in scalar registers).
+struct SegmentWalk {
+  EvenSplit split;
+  int64_t u, u_end, seq_base;
+  int seq, B, HG, max_ctx;
+  const int32_t* context_lens;
+
+  __device__ __forceinline__ bool next(Segment& s) {
+    if (u >= u_end) return false;
+    const int ctx_raw = load_uniform(context_lens, seq);
+    const int nu = context_units(ctx_raw, max_ctx);
+    const int ctx = min(ctx_raw, max_ctx);
+    const int64_t r = u - seq_base;
+    s.seq = seq;
+    s.hg = static_cast<int>(r / nu);
+    const int q_lo = static_cast<int>(r % nu);
+    const int64_t item_first = seq_base + static_cast<int64_t>(s.hg) * nu;
+    s.item_end = item_first + nu;
+    const int64_t seg_end = u_end < s.item_end ? u_end : s.item_end;
+    s.t_lo = q_lo * kDecodeUnitTokens;
+    s.t_hi = min(ctx, (q_lo + static_cast<int>(seg_end - u)) * kDecodeUnitTokens);
+    s.b_lo = s.t_lo / kTokensPerBlock;
+    s.b_hi = (s.t_hi + kTokensPerBlock - 1) / kTokensPerBlock;
+    s.first_owner = split.owner(item_first);
+    s.n_parts = static_cast<int>(split.owner(s.item_end - 1) - s.first_owner + 1);
+    u = seg_end;
+    if (u == s.item_end && s.hg == HG - 1) {  // next sequence with work
+      seq_base = s.item_end;
+      ++seq;
+      while (u < u_end && seq < B - 1 && context_units(load_uniform(context_lens, seq), max_ctx) == 0) ++seq;
+    }
+    return true;
+  }
+};
+
+// Combines the pieces of one split item into its final output, run by one
+// wave: o = sum_j 2^(lse_j - M) o_j / sum_j 2^(lse_j - M), M = max_j lse_j,
+// folded in piece order with a running maximum (so the result does not depend
+// on which workgroup computed which piece). Pieces are read a batch at a time,
+// all loads of a batch in flight together, so a merge costs one memory round
+// trip per batch rather than one per piece.
+// The slot of piece p of an item: a workgroup stores its last segment in slot
+// 2w + 1 and its first one (when it has more than one) in slot 2w; the item's
+// last owner holds it as its first segment unless its range ends inside it.
+__device__ __forceinline__ int64_t piece_slot(const EvenSplit& split, int64_t first_owner, int n_parts, int p,
+                                              int64_t item_end) {
+  const int64_t w = first_owner + p;
+  return p == n_parts - 1 && split.start(w + 1) > item_end ? 2 * w : 2 * w + 1;
 }
 
 template <typename T, int D, int GT>
-__global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void merge_item(const DecodeArgs& a, T* out, int64_t unit0, const EvenSplit& split,
+                                           int64_t first_owner, int n_parts, int64_t item_end, int lane) {
+  constexpr int DL = D / kWave;                             // dims per lane
+  constexpr int NB = GT >= 4 ? 4 : (GT == 2 ? 8 : 16);      // pieces per batch
+  float m[GT], den[GT], num[GT][DL];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    m[g] = -INFINITY;
+    den[g] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < DL; ++k) num[g][k] = 0.0f;
+  }
+  for (int p0 = 0; p0 < n_parts; p0 += NB) {
+    float lv[GT][NB], ov[GT][NB][DL];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int64_t row = piece_slot(split, first_owner, n_parts, min(p0 + j, n_parts - 1), item_end) * GT + g;
+        lv[g][j] = load_agent(a.part_lse + row);
+#pragma unroll
+        for (int k = 0; k < DL; ++k) ov[g][j][k] = load_agent(a.part_out + row * D + k * kWave + lane);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float mn = m[g];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        if (p0 + j < n_parts) mn = fmaxf(mn, lv[g][j]);
+      const float r = exp2_fast(m[g] - mn);
+      den[g] *= r;
+#pragma unroll
+      for (int k = 0; k < DL; ++k) num[g][k] *= r;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (p0 + j < n_parts) {
+          const float f = exp2_fast(lv[g][j] - mn);
+          den[g] += f;
+#pragma unroll
+          for (int k = 0; k < DL; ++k) num[g][k] += f * ov[g][j][k];
+        }
+      }
+      m[g] = mn;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < GT; ++g)
+#pragma unroll
+    for (int k = 0; k < DL; ++k) store_out<T>(out + (unit0 + g) * D + k * kWave + lane, num[g][k] / den[g]);
+}
+
+template <typename T, int D, int GT>
+__global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeArgs a) {
   using S = DecodeShape<T, D>;
   constexpr int W = S::kWords;
   constexpr int E = S::kLaneElems;
+  constexpr int kStride = kDecodeWaves * kChunk;  // tokens between a wave's chunks
+  constexpr int kQVecs = GT * D * Elem<T>::kBytes / 16;  // 16-byte pieces of a group's query rows
+  constexpr int kQPerLane = (kQVecs + kWave - 1) / kWave;
   __shared__ int s_scan[kDecodeThreads];
   __shared__ int s_loc[2];
   __shared__ float s_acc[kDecodeWaves][GT][D];
   __shared__ float s_m[kDecodeWaves][GT];
   __shared__ float s_l[kDecodeWaves][GT];
-  __shared__ int s_last;
+  __shared__ u32x4_t s_q[kDecodeWaves][kQVecs];  // each wave's copy of the segment's query rows
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   // wave index made provably wave-uniform, so per-wave addresses (block-table
   // entries) are scalar loads that do not queue behind the vector loads
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const u32x4_t* sq = s_q[wave];
   const int ts = lane >> 3;  // token slot within a chunk (and ts + 8)
   const int sl = lane & 7;   // sub-lane: which 16-byte pieces of the row
   const int B = a.num_seqs;
@@ -286,7 +434,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
   int mine = 0;
   for (int k = 0; k < per; ++k) {
     const int i = tid * per + k;
-    if (i < B) mine += context_blocks(a.context_lens[i], a.max_context_len);
+    if (i < B) mine += context_units(a.context_lens[i], a.max_context_len);
   }
   s_scan[tid] = mine;
   __syncthreads();
@@ -298,12 +446,15 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
   }
   const int64_t U = static_cast<int64_t>(HG) * __builtin_amdgcn_readfirstlane(s_scan[kDecodeThreads - 1]);
   // With no more workgroups than units every workgroup owns at least one
-  // unit, so the owners of an item's units are consecutive workgroups.
+  // unit, so the owners of an item's units are consecutive workgroups, and
+  // only the first and the last segment of a range can be pieces of items
+  // that other workgroups share.
   const int64_t G = min(static_cast<int64_t>(gridDim.x), U);
   const int w = blockIdx.x;
   if (w >= G) return;
-  const int64_t u_begin = static_cast<int64_t>(w) * U / G;
-  const int64_t u_end = static_cast<int64_t>(w + 1) * U / G;
+  const EvenSplit split{U, G};
+  const int64_t u_begin = split.start(w);
+  const int64_t u_end = split.start(w + 1);
 
   // ---- 2. The sequence holding u_begin: the thread whose sequences span it
   // walks them.
@@ -314,7 +465,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
       int64_t base = lo;
       for (int k = 0; k < per && tid * per + k < B; ++k) {
         const int i = tid * per + k;
-        const int64_t span = static_cast<int64_t>(HG) * context_blocks(a.context_lens[i], a.max_context_len);
+        const int64_t span = static_cast<int64_t>(HG) * context_units(a.context_lens[i], a.max_context_len);
         if (u_begin < base + span) {
           s_loc[0] = i;
           s_loc[1] = static_cast<int>(base / HG);  // blocks of all earlier sequences
@@ -325,73 +476,135 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     }
   }
   __syncthreads();
-  // Values read back from LDS are uniform; say so, so that the whole walk
-  // (and every block-table lookup) stays in scalar registers.
-  int seq = __builtin_amdgcn_readfirstlane(s_loc[0]);
-  int64_t seq_base = static_cast<int64_t>(HG) * __builtin_amdgcn_readfirstlane(s_loc[1]);  // first unit of seq
+  SegmentWalk walk;
+  walk.u = u_begin;
+  walk.u_end = u_end;
+  // values read back from LDS are uniform; say so, so that the walk stays in
+  // scalar registers
+  walk.seq_base = static_cast<int64_t>(HG) * __builtin_amdgcn_readfirstlane(s_loc[1]);
+  walk.seq = __builtin_amdgcn_readfirstlane(s_loc[0]);
+  walk.split = split;
+  walk.B = B;
+  walk.HG = HG;
+  walk.max_ctx = a.max_context_len;
+  walk.context_lens = a.context_lens;
 
   const int64_t row_stride = static_cast<int64_t>(a.num_kv_heads) * D;
   const float sc = a.scale_log2;
   T* out = static_cast<T*>(a.out);
+  const T* q = static_cast<const T*>(a.q);
+  const T* k_cache = static_cast<const T*>(a.k_cache);
+  const T* v_cache = static_cast<const T*>(a.v_cache);
   LaneState<GT, E> st;
 
-  // ---- 3. Walk the segments (pieces of items) in [u_begin, u_end).
-  int64_t u = u_begin;
-  while (u < u_end) {
-    const int ctx_raw = __builtin_amdgcn_readfirstlane(a.context_lens[seq]);
-    const int nb = context_blocks(ctx_raw, a.max_context_len);
-    const int ctx = min(ctx_raw, a.max_context_len);
-    const int64_t r = u - seq_base;
-    const int hg = static_cast<int>(r / nb);
-    const int b_lo = static_cast<int>(r % nb);
-    const int64_t item_first = seq_base + static_cast<int64_t>(hg) * nb;
-    const int64_t item_end = item_first + nb;
-    const int64_t seg_end = u_end < item_end ? u_end : item_end;
-    const int b_hi = b_lo + static_cast<int>(seg_end - u);
-    const int t_lo = b_lo * kTokensPerBlock;
-    const int t_hi = min(ctx, b_hi * kTokensPerBlock);
-
-    const int kvh = hg / groups_per_kv;
-    const int hq0 = kvh * group + (hg % groups_per_kv) * GT;
-    uint32_t qw[GT][W];
-    const T* qbase = static_cast<const T*>(a.q) + (static_cast<int64_t>(seq) * a.num_q_heads + hq0) * D;
+  // ---- 3. Stream the segments. While a segment streams, the next one's
+  // block-table window and query rows are already loading, and the tail of
+  // the segment issues the next segment's first chunk, so no wave drains its
+  // loads between segments. A wave with no token in a (short) segment takes
+  // one chunk at the segment's first row with every token masked, so every
+  // wave runs the same steps.
+  Segment cs;
+  walk.next(cs);  // the range is never empty
+  BlockWindow bw;
+  bw.table = a.block_tables + static_cast<int64_t>(cs.seq) * a.max_blocks_per_seq;
+  bw.limit = cs.b_hi;
+  u32x4_t qv[kQPerLane];
+  {
+    const int hq0 = (cs.hg / groups_per_kv) * group + (cs.hg % groups_per_kv) * GT;
+    const u32x4_t* qsrc = reinterpret_cast<const u32x4_t*>(q + (static_cast<int64_t>(cs.seq) * a.num_q_heads + hq0) * D);
 #pragma unroll
-    for (int g = 0; g < GT; ++g) load_row<T, D>(qbase + g * D, sl, qw[g]);
-    const T* kpool = static_cast<const T*>(a.k_cache) + static_cast<int64_t>(kvh) * D;
-    const T* vpool = static_cast<const T*>(a.v_cache) + static_cast<int64_t>(kvh) * D;
-    BlockWindow bw;
-    bw.table = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks_per_seq;
-    bw.limit = b_hi;
-    bw.fill(b_lo, lane);
+    for (int k = 0; k < kQPerLane; ++k)
+      if (k * kWave + lane < kQVecs) qv[k] = qsrc[k * kWave + lane];
+  }
+  bw.fill(cs.b_lo, lane);  // waits for the query rows too
+#pragma unroll
+  for (int k = 0; k < kQPerLane; ++k)
+    if (k * kWave + lane < kQVecs) s_q[wave][k * kWave + lane] = qv[k];
 
-    // The 4 waves take 16-token chunks round-robin; each wave keeps the next
-    // chunk's loads in flight while it works on the current one.
-    st.reset();
+  Chunk<W> cur, nxt;
+  int c0;     // this wave's current chunk position
+  int t_end;  // tokens before t_end are unmasked for this wave (t_lo for a dummy chunk)
+  int left;   // chunks of this wave in the segment, at least one
+  {
+    const int c = cs.t_lo + wave * kChunk;
+    const bool real = c < cs.t_hi;
+    c0 = real ? c : cs.t_lo;
+    t_end = real ? cs.t_hi : cs.t_lo;
+    left = real ? (cs.t_hi - c + kStride - 1) / kStride : 1;
+    const int kvh = cs.hg / groups_per_kv;
+    load_chunk<T, D>(cur, k_cache + kvh * D, v_cache + kvh * D, bw.get(c0 / kTokensPerBlock, lane), row_stride, c0,
+                     cs.t_hi, ts, sl);
+  }
+
+  // Split-item pieces this workgroup stores (at most the first and the last
+  // segment), counted at the end: item index, piece count, first output row.
+  int pend_item[2] = {-1, -1};
+  int pend_n[2] = {0, 0};
+  int64_t pend_unit0[2] = {0, 0};
+  int64_t pend_first[2] = {0, 0};
+  int64_t pend_end[2] = {0, 0};
+
+  while (true) {
+    const int kvh = cs.hg / groups_per_kv;
+    const int hq0 = kvh * group + (cs.hg % groups_per_kv) * GT;
+    const T* kpool = k_cache + static_cast<int64_t>(kvh) * D;
+    const T* vpool = v_cache + static_cast<int64_t>(kvh) * D;
+
+    // The next segment (or, after the last one, this segment again, so that
+    // the loads below are issued on every path): its block-table window and
+    // query rows start loading now.
+    Segment ns;
+    const bool has_next = walk.next(ns);
+    if (!has_next) ns = cs;
+    BlockWindow bwn;
+    bwn.table = a.block_tables + static_cast<int64_t>(ns.seq) * a.max_blocks_per_seq;
+    bwn.limit = ns.b_hi;
+    bwn.fill_async(ns.b_lo, lane);
+    const int n_kvh = ns.hg / groups_per_kv;
+    const int n_hq0 = n_kvh * group + (ns.hg % groups_per_kv) * GT;
     {
-      // The next chunk's loads are always issued (past the end they re-read
-      // the wave's last chunk, which the L2 still holds), so the number of
-      // loads in flight at each consume is the same on every path and the
-      // wait before it covers only the chunk being consumed.
-      constexpr int kStride = kDecodeWaves * kChunk;
-      int c0 = t_lo + wave * kChunk;
-      if (c0 < t_hi) {
-        const int c_last = c0 + (t_hi - 1 - c0) / kStride * kStride;
-        Chunk<W> cur, nxt;
-        load_chunk<T, D>(cur, kpool, vpool, bw.get(c0 / kTokensPerBlock, lane), row_stride, c0, t_hi, ts, sl);
-        while (true) {
-          int cn = min(c0 + kStride, c_last);
-          load_chunk<T, D>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, t_hi, ts, sl);
-          consume_chunk<T, D, GT>(st, cur, qw, c0 + ts < t_hi, c0 + 8 + ts < t_hi, sc);
-          c0 += kStride;
-          if (c0 >= t_hi) break;
-          cn = min(c0 + kStride, c_last);
-          load_chunk<T, D>(cur, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, t_hi, ts, sl);
-          consume_chunk<T, D, GT>(st, nxt, qw, c0 + ts < t_hi, c0 + 8 + ts < t_hi, sc);
-          c0 += kStride;
-          if (c0 >= t_hi) break;
-        }
-      }
+      const u32x4_t* qsrc =
+          reinterpret_cast<const u32x4_t*>(q + (static_cast<int64_t>(ns.seq) * a.num_q_heads + n_hq0) * D);
+#pragma unroll
+      for (int k = 0; k < kQPerLane; ++k)
+        if (k * kWave + lane < kQVecs) qv[k] = qsrc[k * kWave + lane];
     }
+    const int nc = ns.t_lo + wave * kChunk;
+    const bool n_real = has_next && nc < ns.t_hi;
+    const int n_c0 = n_real ? nc : ns.t_lo;
+
+    // This segment's chunks: whole pairs while at least three remain, then
+    // the last one or two, overlapping the next segment's first chunk. The
+    // loop has a single exit at its head, so every path into a consume has
+    // the same loads in flight and the compiler's wait before it covers that
+    // chunk only.
+    st.reset();
+    int cn = c0;
+    while (left > 2) {
+      cn += kStride;
+      load_chunk<T, D>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi, ts, sl);
+      consume_chunk<T, D, GT>(st, cur, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc);
+      c0 += kStride;
+      cn += kStride;
+      load_chunk<T, D>(cur, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi, ts, sl);
+      consume_chunk<T, D, GT>(st, nxt, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc);
+      c0 += kStride;
+      left -= 2;
+    }
+    // The last two chunk slots. With one chunk left, the second slot re-reads
+    // the first one's rows (a recent read) with every token masked: the tail
+    // then has one shape, with every load issued on every path, so the
+    // next segment's first chunk lands straight in `cur` and nothing waits
+    // for it before the next segment.
+    const T* n_kpool = k_cache + static_cast<int64_t>(n_kvh) * D;
+    const T* n_vpool = v_cache + static_cast<int64_t>(n_kvh) * D;
+    const bool two = left == 2;
+    cn = two ? cn + kStride : cn;
+    load_chunk<T, D>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi, ts, sl);
+    consume_chunk<T, D, GT>(st, cur, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc);
+    c0 += kStride;
+    load_chunk<T, D>(cur, n_kpool, n_vpool, bwn.get(n_c0 / kTokensPerBlock, lane), row_stride, n_c0, ns.t_hi, ts, sl);
+    consume_chunk<T, D, GT>(st, nxt, sq, sl, two && c0 + ts < t_end, two && c0 + 8 + ts < t_end, sc);
 
     // Merge the 8 lane groups of each wave (lane distance 8, 16, 32) ...
 #pragma unroll
@@ -424,10 +637,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     }
     __syncthreads();
 
-    const int64_t unit0 = static_cast<int64_t>(seq) * a.num_q_heads + hq0;
-    const int first_owner = owner_of(item_first, U, G);
-    const int n_parts = owner_of(item_end - 1, U, G) - first_owner + 1;
-    const int part = w - first_owner;
+    const int64_t unit0 = static_cast<int64_t>(cs.seq) * a.num_q_heads + hq0;
     for (int o = tid; o < GT * D; o += kDecodeThreads) {
       const int g = o / D;
       const int d = o % D;
@@ -442,63 +652,73 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
         den += f * s_l[k][g];
       }
       const float val = num / den;
-      if (n_parts == 1) {
+      if (cs.n_parts == 1) {
         store_out<T>(out + (unit0 + g) * D + d, val);
       } else {
-        const int64_t slot = (unit0 + g) * a.max_parts + part;
-        store_agent(a.part_out + slot * D + d, val);
-        if (d == 0) store_agent(a.part_lse + slot, mx + __log2f(den));
+        // A piece of a split item: its normalised output and log2-sum-exp go
+        // to the piece's slot, written through to the device-coherent level
+        // (the merging wave may run on another XCD).
+        const int64_t row = (2 * static_cast<int64_t>(w) + (has_next ? 0 : 1)) * GT + g;
+        store_agent(a.part_out + row * D + d, val);
+        if (d == 0) store_agent(a.part_lse + row, mx + __log2f(den));
       }
     }
-
-    if (n_parts > 1) {
-      // Split item: the last workgroup to finish its piece merges all the
-      // pieces' partial results, in piece order.
-      wait_vector_memory();
-      __syncthreads();
-      if (tid == 0) {
-        int* ctr = a.counters + static_cast<int64_t>(seq) * HG + hg;
-        const int prev = add_agent(ctr, 1);
-        const int last = prev == n_parts - 1;
-        if (last) store_agent_int(ctr, 0);
-        s_last = last;
-      }
-      __syncthreads();
-      if (s_last) {
-        for (int o = tid; o < GT * D; o += kDecodeThreads) {
-          const int g = o / D;
-          const int d = o % D;
-          const int64_t base = (unit0 + g) * a.max_parts;
-          float mx = -INFINITY;
-          for (int p = 0; p < n_parts; ++p) mx = fmaxf(mx, load_agent(a.part_lse + base + p));
-          float num = 0.0f, den = 0.0f;
-          for (int p = 0; p < n_parts; ++p) {
-            const float f = exp2_fast(load_agent(a.part_lse + base + p) - mx);
-            num += f * load_agent(a.part_out + (base + p) * D + d);
-            den += f;
-          }
-          store_out<T>(out + (unit0 + g) * D + d, num / den);
-        }
-      }
+    if (cs.n_parts > 1) {
+      const int k = pend_item[0] < 0 ? 0 : 1;
+      pend_item[k] = cs.seq * HG + cs.hg;
+      pend_n[k] = cs.n_parts;
+      pend_unit0[k] = unit0;
+      pend_first[k] = cs.first_owner;
+      pend_end[k] = cs.item_end;
     }
     __syncthreads();  // LDS is reused by the next segment
 
-    u = seg_end;
-    if (u == item_end && hg == HG - 1) {  // next sequence with work
-      seq_base = item_end;
-      ++seq;
-      while (u < u_end && seq < B - 1 &&
-             context_blocks(__builtin_amdgcn_readfirstlane(a.context_lens[seq]), a.max_context_len) == 0)
-        ++seq;
+    if (!has_next) break;
+    cs = ns;
+    bw = bwn;
+    // the wave's own LDS copy of the query rows: its last read of the old
+    // rows came before this point in the wave's program order
+#pragma unroll
+    for (int k = 0; k < kQPerLane; ++k)
+      if (k * kWave + lane < kQVecs) s_q[wave][k * kWave + lane] = qv[k];
+    c0 = n_c0;
+    t_end = n_real ? ns.t_hi : ns.t_lo;
+    left = n_real ? (ns.t_hi - nc + kStride - 1) / kStride : 1;
+  }
+
+  // ---- 4. Count the stored pieces once this wave's stores are complete:
+  // each wave counts its own share, and an item is complete at kDecodeWaves
+  // counts per piece. The wave whose count completes an item merges its
+  // pieces in piece order, so the result does not depend on timing.
+  if (pend_item[0] >= 0) {
+    wait_vector_memory();
+    // lanes 0 and 1 count the two pieces with one instruction
+    const int mine_item = lane == 0 ? pend_item[0] : pend_item[1];
+    int t = 0;
+    if (lane < 2 && mine_item >= 0) t = add_agent(a.counters + mine_item, 1);
+    const int t0 = __builtin_amdgcn_readlane(t, 0);
+    const int t1 = __builtin_amdgcn_readlane(t, 1);
+    if (t0 == kDecodeWaves * pend_n[0] - 1) {
+      merge_item<T, D, GT>(a, out, pend_unit0[0], split, pend_first[0], pend_n[0], pend_end[0], lane);
+      if (lane == 0) store_agent_int(a.counters + pend_item[0], 0);
+    }
+    if (pend_item[1] >= 0 && t1 == kDecodeWaves * pend_n[1] - 1) {
+      merge_item<T, D, GT>(a, out, pend_unit0[1], split, pend_first[1], pend_n[1], pend_end[1], lane);
+      if (lane == 0) store_agent_int(a.counters + pend_item[1], 0);
     }
   }
 }
 
+// The library's grid: two workgroups per compute unit (more resident
+// workgroups do not stream faster).
+constexpr int kDecodePerCu = 2;
+
 template <typename T, int D, int GT>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   int wgs = a.num_workgroups;
-  if (wgs <= 0) wgs = resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, GT>),
-                                          kDecodeThreads, a.max_units);
+  if (wgs <= 0)
+    wgs = min(kDecodeMaxWorkgroups, resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, GT>),
+                                                        kDecodeThreads, a.max_units, kDecodePerCu));
   paged_decode_kernel<T, D, GT><<<dim3(static_cast<uint32_t>(wgs)), dim3(kDecodeThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
@@ -507,11 +727,14 @@ template <typename T, int D>
 int default_grid(int group, int64_t max_units) {
   switch (decode_head_group(group)) {
     case 4:
-      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 4>), kDecodeThreads, max_units);
+      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 4>), kDecodeThreads,
+                                 max_units, kDecodePerCu);
     case 2:
-      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 2>), kDecodeThreads, max_units);
+      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 2>), kDecodeThreads,
+                                 max_units, kDecodePerCu);
     default:
-      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 1>), kDecodeThreads, max_units);
+      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 1>), kDecodeThreads,
+                                 max_units, kDecodePerCu);
   }
 }
 
@@ -539,9 +762,12 @@ hipError_t launch_decode(const DecodeArgs& a, Dtype dtype, int32_t head_dim, hip
 }
 
 int decode_default_workgroups(Dtype dtype, int32_t head_dim, int32_t group, int64_t max_units) {
-  if (dtype == Dtype::kBF16) return head_dim == 128 ? default_grid<bf16_t, 128>(group, max_units)
-                                                    : default_grid<bf16_t, 64>(group, max_units);
-  return head_dim == 128 ? default_grid<float, 128>(group, max_units) : default_grid<float, 64>(group, max_units);
+  int n;
+  if (dtype == Dtype::kBF16)
+    n = head_dim == 128 ? default_grid<bf16_t, 128>(group, max_units) : default_grid<bf16_t, 64>(group, max_units);
+  else
+    n = head_dim == 128 ? default_grid<float, 128>(group, max_units) : default_grid<float, 64>(group, max_units);
+  return min(n, kDecodeMaxWorkgroups);
 }
 
 }  // namespace pa

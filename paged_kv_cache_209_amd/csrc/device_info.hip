@@ -25,7 +25,7 @@ int g_used = 0;
 
 }  // namespace
 
-int resident_workgroups(const void* kernel, int threads, int64_t max_units) {
+int resident_workgroups(const void* kernel, int threads, int64_t max_units, int max_per_cu, int* compute_units) {
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) device = 0;
   int per_cu = 0, cus = 0;
@@ -47,6 +47,8 @@ int resident_workgroups(const void* kernel, int threads, int64_t max_units) {
       if (g_used < kCacheSlots) g_cache[g_used++] = Entry{kernel, device, per_cu, cus};
     }
   }
+  if (max_per_cu > 0 && per_cu > max_per_cu) per_cu = max_per_cu;
+  if (compute_units != nullptr) *compute_units = cus;
   int64_t wgs = static_cast<int64_t>(per_cu) * cus;
   if (max_units > 0 && wgs > max_units) wgs = max_units;
   return static_cast<int>(wgs < 1 ? 1 : wgs);

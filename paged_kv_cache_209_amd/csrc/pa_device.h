@@ -87,6 +87,15 @@ __device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
   return __shfl_xor(x, mask, kWave);
 }
 
+// A read-only int32 read at a wave-uniform index, through the constant
+// address space, so that it is a scalar load: it waits on the scalar-memory
+// counter, never on the queue of vector loads in flight. Only for arrays that
+// no kernel of this library writes (sequence lengths, offsets).
+__device__ __forceinline__ int load_uniform(const int32_t* p, int64_t i) {
+  using ConstPtr = const __attribute__((address_space(4))) int32_t*;
+  return ((ConstPtr)p)[i];
+}
+
 // Split-context partial results cross workgroups (and XCDs, whose L2 caches
 // are not coherent with each other). They are written and read with
 // agent-scope atomic stores/loads, which are coherent by themselves, so no

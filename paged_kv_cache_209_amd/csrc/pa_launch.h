@@ -23,14 +23,20 @@ struct DecodeArgs {
   int32_t num_kv_heads;
   int32_t max_blocks_per_seq;
   int32_t max_context_len;
-  int32_t num_workgroups;  // the context work is split evenly over this many (0: one resident round)
+  int32_t num_workgroups;  // the context work is split evenly over this many (0: the library's grid)
   int64_t max_units;       // upper bound of the work units (the grid never exceeds it)
-  int32_t max_parts;       // row stride of the partial-result arrays
   float scale_log2;   // scale * log2(e): scores are kept in base-2 units
-  int32_t* counters;  // [num_seqs * num_q_heads], zero between calls
-  float* part_lse;    // [num_seqs * num_q_heads * max_parts]
-  float* part_out;    // [num_seqs * num_q_heads * max_parts * head_dim]
+  int32_t* counters;  // [num_seqs * num_q_heads]: counted pieces of each split item; zero between calls
+  float* part_lse;    // [2 * kDecodeMaxWorkgroups][group]: log2-sum-exp of each stored piece
+  float* part_out;    // [2 * kDecodeMaxWorkgroups][group][head_dim]: normalised output of each piece
 };
+
+// Decode work unit: 64 tokens of one (sequence, query-head group).
+constexpr int32_t kDecodeUnitTokens = 64;
+// Largest decode grid; a workgroup stores at most two split pieces (its
+// first and its last segment), in slots 2w and 2w + 1.
+constexpr int32_t kDecodeMaxWorkgroups = 2048;
+constexpr int32_t kDecodeMaxGroup = 4;  // query heads per decode workgroup
 
 hipError_t launch_decode(const DecodeArgs& args, Dtype dtype, int32_t head_dim, hipStream_t stream);
 
@@ -38,9 +44,12 @@ hipError_t launch_decode(const DecodeArgs& args, Dtype dtype, int32_t head_dim, 
 int decode_default_workgroups(Dtype dtype, int32_t head_dim, int32_t group, int64_t max_units);
 
 // Workgroups of `kernel` (with `threads` per workgroup) that are resident on
-// the current device at once: occupancy per compute unit times compute units,
-// capped by `max_units` (queried once per kernel and device, then cached).
-int resident_workgroups(const void* kernel, int threads, int64_t max_units);
+// the current device at once: occupancy per compute unit (at most
+// `max_per_cu` when that is positive) times compute units, capped by
+// `max_units` (queried once per kernel and device, then cached). The number
+// of compute units is stored in `*compute_units` when that is not null.
+int resident_workgroups(const void* kernel, int threads, int64_t max_units, int max_per_cu = 0,
+                        int* compute_units = nullptr);
 
 // Query heads handled together by one decode workgroup (they share one KV
 // head's rows): the largest of 4, 2, 1 that divides the GQA group size.
@@ -80,23 +89,31 @@ constexpr int64_t kPrefillSlotRows = 2 * 512 * 128;
 
 hipError_t launch_prefill(const PrefillArgs& args, int32_t head_dim, hipStream_t stream);
 
-// Workspace layout shared by the split-context paths: an int32 counter array,
-// padded to 256 bytes, then fp32 log-sum-exp values, then fp32 partial outputs.
+// Workspace layout of the split-context paths: fp32 log-sum-exp values and
+// fp32 partial outputs in regions of a fixed size (sized for the largest head
+// dimension), then the int32 counters. The counters therefore start at the
+// same offset for every call, whatever its sizes, and only ever share bytes
+// with other calls' counters, which every call leaves zero: a workspace
+// zero-filled once stays valid for any sequence of calls of one entry point.
+constexpr int64_t kMaxHeadDim = 128;
+
 struct WorkspaceLayout {
-  size_t counters_bytes;
-  size_t lse_bytes;
-  size_t out_bytes;
-  size_t total() const { return counters_bytes + lse_bytes + out_bytes; }
+  size_t lse_off, out_off, counters_off, total;
 };
 
-inline WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, int64_t rows_per_seq,
-                                        int64_t max_parts) {
+inline WorkspaceLayout make_workspace_layout(int64_t slot_rows, int64_t counters) {
   WorkspaceLayout w;
-  const int64_t units = num_seqs * num_q_heads * rows_per_seq;
-  w.counters_bytes = static_cast<size_t>(((num_seqs * num_q_heads * 4) + 255) / 256 * 256);
-  w.lse_bytes = static_cast<size_t>((units * max_parts * 4 + 255) / 256 * 256);
-  w.out_bytes = static_cast<size_t>(units * max_parts * head_dim * 4);
+  w.lse_off = 0;
+  w.out_off = static_cast<size_t>((slot_rows * 4 + 255) / 256 * 256);
+  w.counters_off = w.out_off + static_cast<size_t>(slot_rows * kMaxHeadDim * 4);
+  w.total = w.counters_off + static_cast<size_t>(counters * 4);
   return w;
+}
+
+// Decode: two piece slots per workgroup of the largest grid, each for up to
+// kDecodeMaxGroup query heads; one counter per (sequence, query head).
+inline WorkspaceLayout decode_workspace_layout(int64_t num_seqs, int64_t num_q_heads) {
+  return make_workspace_layout(int64_t{2} * kDecodeMaxWorkgroups * kDecodeMaxGroup, num_seqs * num_q_heads);
 }
 
 }  // namespace pa

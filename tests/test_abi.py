@@ -88,12 +88,17 @@ def test_decode_empty_batch_is_noop():
 
 
 def test_decode_workspace_sizing():
-    assert pa.decode_workspace_bytes(4, 8, 128, 256) == 0
-    need = pa.decode_workspace_bytes(4, 8, 128, 4096)
-    # counters (padded) + lse + partial outputs for 16 partitions of 256 tokens
-    assert need >= 4 * 8 * 16 * (128 + 1) * 4
+    # one 64-token work unit per context: nothing is ever split
+    assert pa.decode_workspace_bytes(4, 8, 128, 64) == 0
+    need = pa.decode_workspace_bytes(4, 8, 128, 65)
+    # counters (padded) + two piece slots per workgroup of the largest grid
+    # (2048), each for up to 4 query heads: lse values and partial outputs
+    assert need >= 2 * 2048 * 4 * (128 + 1) * 4
+    # independent of the context length
+    assert pa.decode_workspace_bytes(4, 8, 128, 1 << 20) == need
     assert dec(ws=P, wsb=need - 1) == WS
     assert dec(ws=P, wsb=need - 1, part=7) == WS
+    assert dec(ws=P, wsb=need, part=2049) == INVALID
     n = pa.decode_num_workgroups(64, 16, 8, 128, 4096)
     assert 1 <= n <= 64 * 8 * 16
     assert pa.decode_num_workgroups(1, 2, 1, 64, 1, torch.float32) == 1

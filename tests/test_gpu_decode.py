@@ -194,3 +194,25 @@ def test_longest_context_fills_table():
     c = ragged_case(14, [16384, 1], 8, 2, 128, torch.bfloat16, poison=True)
     ref = oracle.paged_attn_decode(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.scale)
     compare(run_decode(c), ref, torch.bfloat16)
+
+
+def test_workspace_reused_across_sizes():
+    """One workspace, zero-filled once, serves calls of different sizes in any
+    order: a later call's counters never fall on bytes an earlier call used
+    for partial results (the counters sit after fixed-size partial regions)."""
+    say("decode workspace reuse")
+    lengths = [1, 300, 700, 1000, 1537, 2900]
+    few = ragged_case(21, lengths, 8, 8, 128, torch.bfloat16)          # 6 x 8 counters
+    many = ragged_case(22, lengths * 3, 12, 4, 64, torch.bfloat16)     # 18 x 12 counters, another head_dim
+    need = max(pa.decode_workspace_bytes(c.num_seqs, c.num_q_heads, c.head_dim, c.max_context_len)
+               for c in (few, many))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for c in (few, many, few, many):
+        ref = oracle.paged_attn_decode(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.scale)
+        q = to_dev(c.q)
+        out = torch.empty_like(q)
+        pa.paged_attn_decode(out, q, to_dev(c.k_cache), to_dev(c.v_cache), to_dev(c.block_tables),
+                             to_dev(c.context_lens), c.scale, c.max_context_len, num_workgroups=333,
+                             workspace_tensor=ws)
+        torch.cuda.synchronize()
+        compare(out, ref, torch.bfloat16)

@@ -181,3 +181,23 @@ def test_empty_and_zero_length_sequences():
                           torch.zeros((1,), dtype=torch.int32, device=DEV),
                           torch.zeros((2,), dtype=torch.int32, device=DEV), 0.1, 0, 1)
     torch.cuda.synchronize()
+
+
+def test_workspace_reused_across_sizes():
+    """One prefill workspace, zero-filled once, serves calls of different sizes
+    in any order (the counters sit after fixed-size partial regions)."""
+    say("prefill workspace reuse")
+    few = w.build_prefill_case("pf_few", [300, 1500], [5, 3], 8, 8, 128, torch.bfloat16, 31, with_slots=False)
+    many = w.build_prefill_case("pf_many", [1000, 17, 2047, 256, 640, 3000], [40, 300, 5, 64, 2, 9], 12, 4, 64,
+                                torch.bfloat16, 32, with_slots=False)
+    need = max(pa.prefill_workspace_bytes(len(c.context_lens), c.q.shape[1], c.q.shape[2], c.max_q_len,
+                                          c.max_context_len) for c in (few, many))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for c in (few, many, few, many):
+        q = to_dev(c.q)
+        out = torch.empty_like(q)
+        pa.paged_attn_prefill(out, q, to_dev(c.k), to_dev(c.v), to_dev(c.k_cache), to_dev(c.v_cache),
+                              to_dev(c.block_tables), to_dev(c.context_lens), to_dev(c.cu_seqlens), c.scale,
+                              c.max_q_len, c.max_context_len, workspace_tensor=ws)
+        torch.cuda.synchronize()
+        compare(out, oracle_prefill(c), torch.bfloat16)
