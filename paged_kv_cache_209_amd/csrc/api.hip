@@ -30,8 +30,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 pa_status to_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-// Upper bound of decode work units: one per 64 tokens of the longest
-// context, for every (sequence, query-head group).
+// Upper bound of the decode work units that hold tokens (one per 64 tokens
+// of the longest context, for every (sequence, query-head group)): the
+// library's grid never exceeds it.
 int64_t decode_max_units(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len) {
   const int64_t head_groups = num_q_heads / pa::decode_head_group(num_q_heads / num_kv_heads);
   return static_cast<int64_t>(num_seqs) * head_groups * ceil_div(max_context_len, pa::kDecodeUnitTokens);

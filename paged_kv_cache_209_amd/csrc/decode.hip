@@ -274,10 +274,21 @@ __device__ __forceinline__ int context_units(int ctx, int max_ctx) {
   return (ctx + kDecodeUnitTokens - 1) / kDecodeUnitTokens;
 }
 
-// The U work units are split into G equal contiguous ranges, one per
-// workgroup: workgroup w owns [start(w), start(w + 1)). With G <= U every
-// range is non-empty, so the owners of an item's units are consecutive
-// workgroups.
+// The U cost units are split into G equal contiguous ranges, one per
+// workgroup: workgroup w owns [start(w), start(w + 1)). An item costs one
+// unit per 64 tokens of context plus kItemCost units ahead of them that hold
+// no tokens: they stand for the fixed work of finishing a segment (the
+// cross-wave merge and its barriers), so ranges of many short items carry
+// fewer tokens and all ranges take about the same time. The owners of an
+// item's real units are consecutive workgroups.
+constexpr int kItemCost = kDecodeItemCost;
+
+// Cost units of one item of a sequence (none for an empty context).
+__device__ __forceinline__ int item_cost(int ctx, int max_ctx) {
+  const int nu = context_units(ctx, max_ctx);
+  return nu > 0 ? nu + kItemCost : 0;
+}
+
 struct EvenSplit {
   int64_t U, G;
   __device__ __forceinline__ int64_t start(int64_t w) const { return U * w / G; }
@@ -288,11 +299,11 @@ struct EvenSplit {
 // unit range: the tokens it covers and the blocks that hold them.
 struct Segment {
   int seq, hg;
-  int t_lo, t_hi;       // tokens [t_lo, t_hi)
-  int b_lo, b_hi;       // blocks [b_lo, b_hi) holding them
-  int n_parts;          // pieces of the item over all workgroups
-  int64_t first_owner;  // workgroup holding the item's first piece
-  int64_t item_end;     // one past the item's last unit
+  int t_lo, t_hi;        // tokens [t_lo, t_hi)
+  int b_lo, b_hi;        // blocks [b_lo, b_hi) holding them
+  int n_parts;           // pieces of the item over all workgroups
+  int64_t first_owner;   // workgroup holding the item's first piece
+  int64_t item_first;    // the item's first cost unit (a virtual one)
 };
 
 // Walks the segments of the unit range [u, u_end) in order. All its state is
@@ -303,31 +314,41 @@ struct SegmentWalk {
   int seq, B, HG, max_ctx;
   const int32_t* context_lens;
 
+  // The next segment with tokens, if any is left in the range.
   __device__ __forceinline__ bool next(Segment& s) {
-    if (u >= u_end) return false;
-    const int ctx_raw = load_uniform(context_lens, seq);
-    const int nu = context_units(ctx_raw, max_ctx);
-    const int ctx = min(ctx_raw, max_ctx);
-    const int64_t r = u - seq_base;
-    s.seq = seq;
-    s.hg = static_cast<int>(r / nu);
-    const int q_lo = static_cast<int>(r % nu);
-    const int64_t item_first = seq_base + static_cast<int64_t>(s.hg) * nu;
-    s.item_end = item_first + nu;
-    const int64_t seg_end = u_end < s.item_end ? u_end : s.item_end;
-    s.t_lo = q_lo * kDecodeUnitTokens;
-    s.t_hi = min(ctx, (q_lo + static_cast<int>(seg_end - u)) * kDecodeUnitTokens);
-    s.b_lo = s.t_lo / kTokensPerBlock;
-    s.b_hi = (s.t_hi + kTokensPerBlock - 1) / kTokensPerBlock;
-    s.first_owner = split.owner(item_first);
-    s.n_parts = static_cast<int>(split.owner(s.item_end - 1) - s.first_owner + 1);
-    u = seg_end;
-    if (u == s.item_end && s.hg == HG - 1) {  // next sequence with work
-      seq_base = s.item_end;
-      ++seq;
-      while (u < u_end && seq < B - 1 && context_units(load_uniform(context_lens, seq), max_ctx) == 0) ++seq;
+    while (u < u_end) {
+      const int ctx_raw = load_uniform(context_lens, seq);
+      const int nu = context_units(ctx_raw, max_ctx);
+      const int ctx = min(ctx_raw, max_ctx);
+      const int64_t span = nu + kItemCost;  // cost units of one item of this sequence
+      const int64_t r = u - seq_base;
+      const int hg = static_cast<int>(r / span);
+      const int64_t item_first = seq_base + hg * span;
+      const int64_t real_first = item_first + kItemCost;
+      const int64_t item_end = item_first + span;
+      const int64_t seg_end = u_end < item_end ? u_end : item_end;
+      const int64_t lo = u > real_first ? u : real_first;
+      const bool has_tokens = lo < seg_end;
+      if (has_tokens) {
+        s.seq = seq;
+        s.hg = hg;
+        s.t_lo = static_cast<int>(lo - real_first) * kDecodeUnitTokens;
+        s.t_hi = min(ctx, static_cast<int>(seg_end - real_first) * kDecodeUnitTokens);
+        s.b_lo = s.t_lo / kTokensPerBlock;
+        s.b_hi = (s.t_hi + kTokensPerBlock - 1) / kTokensPerBlock;
+        s.first_owner = split.owner(real_first);
+        s.n_parts = static_cast<int>(split.owner(item_end - 1) - s.first_owner + 1);
+        s.item_first = item_first;
+      }
+      u = seg_end;
+      if (u == item_end && hg == HG - 1) {  // next sequence with work
+        seq_base = item_end;
+        ++seq;
+        while (u < u_end && seq < B - 1 && context_units(load_uniform(context_lens, seq), max_ctx) == 0) ++seq;
+      }
+      if (has_tokens) return true;
     }
-    return true;
+    return false;
   }
 };
 
@@ -337,18 +358,20 @@ struct SegmentWalk {
 // on which workgroup computed which piece). Pieces are read a batch at a time,
 // all loads of a batch in flight together, so a merge costs one memory round
 // trip per batch rather than one per piece.
-// The slot of piece p of an item: a workgroup stores its last segment in slot
-// 2w + 1 and its first one (when it has more than one) in slot 2w; the item's
-// last owner holds it as its first segment unless its range ends inside it.
-__device__ __forceinline__ int64_t piece_slot(const EvenSplit& split, int64_t first_owner, int n_parts, int p,
-                                              int64_t item_end) {
+// The slot of piece p of an item: a workgroup stores its first segment in
+// slot 2w and a later one (only its last can be a piece of a split item) in
+// slot 2w + 1. Every piece but the first is its holder's first segment; the
+// first piece is too when its holder's range starts inside the item's
+// virtual units (real units of earlier items would come first otherwise).
+__device__ __forceinline__ int64_t piece_slot(const EvenSplit& split, int64_t first_owner, int p,
+                                              int64_t item_first) {
   const int64_t w = first_owner + p;
-  return p == n_parts - 1 && split.start(w + 1) > item_end ? 2 * w : 2 * w + 1;
+  return p > 0 || split.start(w) >= item_first ? 2 * w : 2 * w + 1;
 }
 
 template <typename T, int D, int GT>
 __device__ __forceinline__ void merge_item(const DecodeArgs& a, T* out, int64_t unit0, const EvenSplit& split,
-                                           int64_t first_owner, int n_parts, int64_t item_end, int lane) {
+                                           int64_t first_owner, int n_parts, int64_t item_first, int lane) {
   constexpr int DL = D / kWave;                             // dims per lane
   constexpr int NB = GT >= 4 ? 4 : (GT == 2 ? 8 : 16);      // pieces per batch
   float m[GT], den[GT], num[GT][DL];
@@ -365,7 +388,7 @@ __device__ __forceinline__ void merge_item(const DecodeArgs& a, T* out, int64_t 
     for (int g = 0; g < GT; ++g) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int64_t row = piece_slot(split, first_owner, n_parts, min(p0 + j, n_parts - 1), item_end) * GT + g;
+        const int64_t row = piece_slot(split, first_owner, min(p0 + j, n_parts - 1), item_first) * GT + g;
         lv[g][j] = load_agent(a.part_lse + row);
 #pragma unroll
         for (int k = 0; k < DL; ++k) ov[g][j][k] = load_agent(a.part_out + row * D + k * kWave + lane);
@@ -434,7 +457,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
   int mine = 0;
   for (int k = 0; k < per; ++k) {
     const int i = tid * per + k;
-    if (i < B) mine += context_units(a.context_lens[i], a.max_context_len);
+    if (i < B) mine += item_cost(a.context_lens[i], a.max_context_len);
   }
   s_scan[tid] = mine;
   __syncthreads();
@@ -465,7 +488,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
       int64_t base = lo;
       for (int k = 0; k < per && tid * per + k < B; ++k) {
         const int i = tid * per + k;
-        const int64_t span = static_cast<int64_t>(HG) * context_units(a.context_lens[i], a.max_context_len);
+        const int64_t span = static_cast<int64_t>(HG) * item_cost(a.context_lens[i], a.max_context_len);
         if (u_begin < base + span) {
           s_loc[0] = i;
           s_loc[1] = static_cast<int>(base / HG);  // blocks of all earlier sequences
@@ -504,7 +527,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
   // one chunk at the segment's first row with every token masked, so every
   // wave runs the same steps.
   Segment cs;
-  walk.next(cs);  // the range is never empty
+  // A range that holds only virtual units has nothing to do.
+  if (!walk.next(cs)) return;
   BlockWindow bw;
   bw.table = a.block_tables + static_cast<int64_t>(cs.seq) * a.max_blocks_per_seq;
   bw.limit = cs.b_hi;
@@ -542,7 +566,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
   int pend_n[2] = {0, 0};
   int64_t pend_unit0[2] = {0, 0};
   int64_t pend_first[2] = {0, 0};
-  int64_t pend_end[2] = {0, 0};
+  int64_t pend_item_first[2] = {0, 0};
+  bool first_seg = true;
 
   while (true) {
     const int kvh = cs.hg / groups_per_kv;
@@ -658,7 +683,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
         // A piece of a split item: its normalised output and log2-sum-exp go
         // to the piece's slot, written through to the device-coherent level
         // (the merging wave may run on another XCD).
-        const int64_t row = (2 * static_cast<int64_t>(w) + (has_next ? 0 : 1)) * GT + g;
+        const int64_t row = (2 * static_cast<int64_t>(w) + (first_seg ? 0 : 1)) * GT + g;
         store_agent(a.part_out + row * D + d, val);
         if (d == 0) store_agent(a.part_lse + row, mx + __log2f(den));
       }
@@ -669,11 +694,12 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
       pend_n[k] = cs.n_parts;
       pend_unit0[k] = unit0;
       pend_first[k] = cs.first_owner;
-      pend_end[k] = cs.item_end;
+      pend_item_first[k] = cs.item_first;
     }
     __syncthreads();  // LDS is reused by the next segment
 
     if (!has_next) break;
+    first_seg = false;
     cs = ns;
     bw = bwn;
     // the wave's own LDS copy of the query rows: its last read of the old
@@ -699,19 +725,20 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
     const int t0 = __builtin_amdgcn_readlane(t, 0);
     const int t1 = __builtin_amdgcn_readlane(t, 1);
     if (t0 == kDecodeWaves * pend_n[0] - 1) {
-      merge_item<T, D, GT>(a, out, pend_unit0[0], split, pend_first[0], pend_n[0], pend_end[0], lane);
+      merge_item<T, D, GT>(a, out, pend_unit0[0], split, pend_first[0], pend_n[0], pend_item_first[0], lane);
       if (lane == 0) store_agent_int(a.counters + pend_item[0], 0);
     }
     if (pend_item[1] >= 0 && t1 == kDecodeWaves * pend_n[1] - 1) {
-      merge_item<T, D, GT>(a, out, pend_unit0[1], split, pend_first[1], pend_n[1], pend_end[1], lane);
+      merge_item<T, D, GT>(a, out, pend_unit0[1], split, pend_first[1], pend_n[1], pend_item_first[1], lane);
       if (lane == 0) store_agent_int(a.counters + pend_item[1], 0);
     }
   }
 }
 
-// The library's grid: two workgroups per compute unit (more resident
-// workgroups do not stream faster).
-constexpr int kDecodePerCu = 2;
+// The library's grid: one workgroup per compute unit. Measured on MI355X, one
+// resident workgroup (one wave per SIMD) streams faster than two: the second
+// workgroup on a CU only adds contention for the same memory path.
+constexpr int kDecodePerCu = 1;
 
 template <typename T, int D, int GT>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {

@@ -31,8 +31,11 @@ struct DecodeArgs {
   float* part_out;    // [2 * kDecodeMaxWorkgroups][group][head_dim]: normalised output of each piece
 };
 
-// Decode work unit: 64 tokens of one (sequence, query-head group).
+// Decode work unit: 64 tokens of one (sequence, query-head group). Each item
+// also costs kDecodeItemCost units that hold no tokens (the fixed work of a
+// segment), so the split over workgroups balances time rather than tokens.
 constexpr int32_t kDecodeUnitTokens = 64;
+constexpr int32_t kDecodeItemCost = 2;
 // Largest decode grid; a workgroup stores at most two split pieces (its
 // first and its last segment), in slots 2w and 2w + 1.
 constexpr int32_t kDecodeMaxWorkgroups = 2048;
