@@ -207,10 +207,15 @@ pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const v
   if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
 
   const int32_t group = num_q_heads / num_kv_heads;
-  const int32_t rows = static_cast<int64_t>(max_q_len) * group <= 32 ? 32 : 128;
-  const int64_t qtiles = ceil_div(static_cast<int64_t>(max_q_len) * group, rows);
-  const int64_t max_units = static_cast<int64_t>(num_seqs) * num_kv_heads * qtiles * ceil_div(max_context_len, 64);
-  const int64_t cap = rows == 128 ? pa::kPrefillMaxWorkgroups128 : pa::kPrefillMaxWorkgroups32;
+  // Query rows per work item: a sequence's (token, head) rows of one KV head
+  // in tiles of 32 (one wave), 128 or 256 (4 or 8 waves sharing each K/V tile).
+  const int64_t seq_rows = static_cast<int64_t>(max_q_len) * group;
+  const int32_t rows = seq_rows <= 32 ? 32 : (seq_rows <= 128 ? 128 : 256);
+  const int64_t qtiles = ceil_div(seq_rows, rows);
+  const int64_t key_tile = 64;  // keys per work unit (the kernels' tile width)
+  const int64_t max_units = static_cast<int64_t>(num_seqs) * num_kv_heads * qtiles * ceil_div(max_context_len, key_tile);
+  const int64_t cap = rows == 256 ? pa::kPrefillMaxWorkgroups256
+                                  : (rows == 128 ? pa::kPrefillMaxWorkgroups128 : pa::kPrefillMaxWorkgroups32);
 
   pa::PrefillArgs a;
   a.out = out;

@@ -77,18 +77,22 @@ struct PrefillArgs {
   int32_t max_context_len;
   float scale_log2;        // |scale * log2(e)|, at least 1e-30 (so that it is positive)
   int32_t negate_q;        // 1 when the scale is negative: q is negated on load
-  int32_t rows_per_tile;   // query rows per item: 128 (4 waves) or 32 (1 wave)
+  int32_t rows_per_tile;   // query rows per item: 256 (8 waves), 128 (4 waves) or 32 (1 wave)
   int32_t num_workgroups;  // the key tiles of all items are split evenly over these
   int32_t* counters;       // [num_seqs * num_q_heads * (max_q_len + 1)], zero between calls
   float* part_lse;         // [2 * num_workgroups * rows_per_tile]
   float* part_out;         // [2 * num_workgroups * rows_per_tile * head_dim]
 };
 
-// Largest grids the prefill launcher uses for each tile height, and the
+// Largest grids the prefill launcher uses for each tile height (one 8-wave
+// workgroup per CU, two 4-wave ones, four 1-wave ones), and the
 // partial-result rows their workspace holds (two pieces per workgroup).
+constexpr int kPrefillMaxWorkgroups256 = 256;
 constexpr int kPrefillMaxWorkgroups128 = 512;
 constexpr int kPrefillMaxWorkgroups32 = 1024;
 constexpr int64_t kPrefillSlotRows = 2 * 512 * 128;
+static_assert(2 * kPrefillMaxWorkgroups256 * 256 <= kPrefillSlotRows, "slot rows");
+static_assert(2 * kPrefillMaxWorkgroups32 * 32 <= kPrefillSlotRows, "slot rows");
 
 hipError_t launch_prefill(const PrefillArgs& args, int32_t head_dim, hipStream_t stream);
 

@@ -43,7 +43,6 @@ namespace pa {
 
 namespace {
 
-constexpr int kKeysPerTile = 64;
 constexpr int kRowsPerWave = 32;
 constexpr float kEmptyMaxP = -1.0e30f;
 constexpr float kSlack = 8.0f;
@@ -51,13 +50,18 @@ constexpr int kNonTemporal = 2;  // cache-policy operand of direct-to-LDS loads:
 
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-template <int D>
+// Shapes for head dim D and key tiles of KT keys (64 on every path here; 32 is
+// supported for experiments with deeper LDS pipelines in the same LDS).
+template <int D, int KT>
 struct PShape {
   static constexpr int kDChunks = D / 32;  // k-steps of the Q.K product
   static constexpr int kDTiles = D / 16;   // 16-row tiles of O^T
   static constexpr int kRowBytes = D * 2;  // one key's head row in LDS (no padding)
   static constexpr int kPieces = D * 2 / 16;  // 16-byte pieces per row
-  static constexpr int kTileBytes = kKeysPerTile * kRowBytes;
+  static constexpr int kTileBytes = KT * kRowBytes;
+  static constexpr int kMt = KT / 16;   // 16-key tiles of S^T
+  static constexpr int kKc2 = KT / 32;  // 32-key steps of O^T += V^T P^T
+  static_assert(KT == 32 || KT == 64, "key tile");
 };
 
 // Swizzled LDS tiles: 16-byte piece c of key row r is stored at slot
@@ -108,11 +112,11 @@ __device__ __forceinline__ SeqGeom seq_geom(const PrefillArgs& a, int i) {
   return s;
 }
 
-// 64-key tiles visible to query tile qt (rows qt*ROWS .. qt*ROWS+ROWS-1).
-template <int ROWS>
+// KT-key tiles visible to query tile qt (rows qt*ROWS .. qt*ROWS+ROWS-1).
+template <int ROWS, int KT>
 __device__ __forceinline__ int tiles_of(const SeqGeom& s, int group, int qt) {
   const int jmax = min(s.n - 1, ((qt + 1) * ROWS - 1) / group);
-  return (s.c + jmax + 1 + kKeysPerTile - 1) / kKeysPerTile;
+  return (s.c + jmax + 1 + KT - 1) / KT;
 }
 
 template <int ROWS>
@@ -120,12 +124,12 @@ __device__ __forceinline__ int qtiles_of(const SeqGeom& s, int group) {
   return (s.n * group + ROWS - 1) / ROWS;
 }
 
-template <int ROWS>
+template <int ROWS, int KT>
 __device__ int units_per_head(const SeqGeom& s, int group) {
   if (s.n <= 0) return 0;
   const int qts = qtiles_of<ROWS>(s, group);
   int u = 0;
-  for (int qt = 0; qt < qts; ++qt) u += tiles_of<ROWS>(s, group, qt);
+  for (int qt = 0; qt < qts; ++qt) u += tiles_of<ROWS, KT>(s, group, qt);
   return u;
 }
 
@@ -146,7 +150,7 @@ __device__ __forceinline__ int owner_of_unit(int64_t u, int64_t U, int64_t G) {
 
 // Where the rows of a key tile come from: the pool (through the block table)
 // for positions below c, the call's k/v for the new tokens.
-template <int D, int NT>
+template <int D, int NT, int KT>
 struct TileSrc {
   const bf16_t* kpool;
   const bf16_t* vpool;
@@ -166,19 +170,19 @@ struct TileSrc {
 // base plus the precomputed lane offsets; a tile that straddles the two, or
 // runs past the last key (its rows re-read the last key), resolves each
 // lane's row on its own.
-template <int D, int NT>
-__device__ __forceinline__ void issue_tile(const TileSrc<D, NT>& t, int kt, char* stage,
-                                           const int (&krow)[kKeysPerTile * PShape<D>::kPieces / NT],
-                                           const int (&kgo)[kKeysPerTile * PShape<D>::kPieces / NT],
-                                           const int (&vgo)[kKeysPerTile * PShape<D>::kPieces / NT], int tid,
+template <int D, int NT, int KT>
+__device__ __forceinline__ void issue_tile(const TileSrc<D, NT, KT>& t, int kt, char* stage,
+                                           const int (&krow)[KT * PShape<D, KT>::kPieces / NT],
+                                           const int (&kgo)[KT * PShape<D, KT>::kPieces / NT],
+                                           const int (&vgo)[KT * PShape<D, KT>::kPieces / NT], int tid,
                                            int wave) {
-  constexpr int kIters = kKeysPerTile * PShape<D>::kPieces / NT;
-  constexpr int TB = PShape<D>::kTileBytes;
-  const int k0 = kt * kKeysPerTile;
+  constexpr int kIters = KT * PShape<D, KT>::kPieces / NT;
+  constexpr int TB = PShape<D, KT>::kTileBytes;
+  const int k0 = kt * KT;
   char* kdst = stage;
   char* vdst = stage + TB;
-  const bool in_pool = k0 + kKeysPerTile <= t.c;
-  const bool in_new = k0 >= t.c && k0 + kKeysPerTile <= t.total;
+  const bool in_pool = k0 + KT <= t.c;
+  const bool in_new = k0 >= t.c && k0 + KT <= t.total;
   if (in_pool || in_new) {
     int64_t row0;
     const bf16_t* kb;
@@ -221,17 +225,106 @@ __device__ __forceinline__ void issue_tile(const TileSrc<D, NT>& t, int kt, char
   }
 }
 
-template <int D, int WM>
-__global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a) {
-  using S = PShape<D>;
+// Merges the pieces of one split item (ROWS query rows of one sequence and KV
+// head) into the output, run by the whole workgroup: row r of the result is
+// sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M), folded in piece order with a
+// running maximum M (a piece whose keys are all causally hidden from a row
+// has lse = -inf and weight 0). Piece p lives in slot 2(first_owner + p), or
+// 2 first_owner + 1 for the first piece when its owner's range starts inside
+// an earlier item. Each thread takes 4 dims of kRowsPerThread rows and keeps
+// the loads of kMergeBatch pieces of a group of rows in flight together.
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void merge_pieces(const PrefillArgs& a, bf16_t* outp, int64_t first_owner, int n_parts,
+                                             bool first_in_late_slot, const SeqGeom& sg, int qt, int h, int group,
+                                             int tid) {
+  constexpr int D4 = D / 4;
+  constexpr int kRowStep = NT / D4;
+  constexpr int kRowsPerThread = ROWS / kRowStep;
+  constexpr int kRowGroup = kRowsPerThread < 8 ? kRowsPerThread : 8;
+  constexpr int kMergeBatch = 2;
+  static_assert(ROWS % kRowStep == 0 && kRowsPerThread % kRowGroup == 0, "merge tiling");
+  const int d4 = tid % D4;
+  const int r0 = tid / D4;
+  for (int rg = 0; rg < kRowsPerThread; rg += kRowGroup) {
+    float m[kRowGroup], den[kRowGroup];
+    f32x4_t num[kRowGroup];
+#pragma unroll
+    for (int k = 0; k < kRowGroup; ++k) {
+      m[k] = -INFINITY;
+      den[k] = 0.0f;
+      num[k] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    for (int p0 = 0; p0 < n_parts; p0 += kMergeBatch) {
+      float lv[kMergeBatch][kRowGroup];
+      f32x4_t ov[kMergeBatch][kRowGroup];
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const int p = min(p0 + j, n_parts - 1);
+        const int64_t slot = 2 * (first_owner + p) + (p == 0 && first_in_late_slot ? 1 : 0);
+        const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(a.part_out + slot * ROWS * D, ROWS * D * 4);
+#pragma unroll
+        for (int k = 0; k < kRowGroup; ++k) {
+          const int row = r0 + (rg + k) * kRowStep;
+          lv[j][k] = load_agent(a.part_lse + slot * ROWS + row);
+          ov[j][k] = load4_agent(pr, (row * D + 4 * d4) * 4);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kRowGroup; ++k) {
+        float mn = m[k];
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j)
+          if (p0 + j < n_parts) mn = fmaxf(mn, lv[j][k]);
+        if (mn == -INFINITY) continue;  // no key of these pieces is visible yet
+        const float r = m[k] == -INFINITY ? 0.0f : exp2_fast(m[k] - mn);
+        den[k] *= r;
+        num[k] *= r;
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+          if (p0 + j < n_parts && lv[j][k] != -INFINITY) {
+            const float f = exp2_fast(lv[j][k] - mn);
+            den[k] += f;
+            num[k] += f * ov[j][k];
+          }
+        }
+        m[k] = mn;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kRowGroup; ++k) {
+      const int R = qt * ROWS + r0 + (rg + k) * kRowStep;
+      const int j = R / group;
+      if (j >= sg.n) continue;
+      const float inv = 1.0f / den[k];
+      const uint32_t lo = pack_bf16x2(num[k][0] * inv, num[k][1] * inv);
+      const uint32_t hi = pack_bf16x2(num[k][2] * inv, num[k][3] * inv);
+      bf16_t* orow = outp + (static_cast<int64_t>(sg.start + j) * a.num_q_heads + h * group + R % group) * D;
+      *reinterpret_cast<uint2*>(orow + 4 * d4) = make_uint2(lo, hi);
+    }
+  }
+}
+
+// LDS stages of [K tile | V tile] per workgroup: the 8-wave workgroup (one
+// per CU) keeps two tiles in flight while it works on a third; the smaller
+// ones (two per CU) keep one. (Three stages of 32-key tiles for the 1-wave
+// verify workgroup, in the same LDS, measured 25% slower on MI355X: the fixed
+// cost per tile outweighs the extra loads in flight.)
+template <int WM>
+constexpr int prefill_stages() {
+  return WM >= 8 ? 3 : 2;
+}
+
+template <int D, int WM, int KT>
+__global__ __launch_bounds__(64 * WM, WM >= 8 ? 1 : 2) void paged_prefill_kernel(PrefillArgs a) {
+  using S = PShape<D, KT>;
   constexpr int ROWS = kRowsPerWave * WM;
   constexpr int NT = kWave * WM;
   constexpr int TB = S::kTileBytes;
-  // Two stages of [K tile | V tile]: tile t+1 streams in while t is used.
-  __shared__ __attribute__((aligned(16))) char s_kv[2][2 * TB];
+  constexpr int kStages = prefill_stages<WM>();
+  constexpr int kAhead = kStages - 1;  // tiles in flight while one is used
+  __shared__ __attribute__((aligned(16))) char s_kv[kStages][2 * TB];
   __shared__ int s_scan[NT];
   __shared__ int s_loc[2];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -249,7 +342,7 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
   int mine = 0;
   for (int k = 0; k < per; ++k) {
     const int i = tid * per + k;
-    if (i < B) mine += Hkv * units_per_head<ROWS>(seq_geom(a, i), group);
+    if (i < B) mine += Hkv * units_per_head<ROWS, KT>(seq_geom(a, i), group);
   }
   s_scan[tid] = mine;
   __syncthreads();
@@ -274,7 +367,7 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
       int64_t base = lo;
       for (int k = 0; k < per && tid * per + k < B; ++k) {
         const int i = tid * per + k;
-        const int64_t span = static_cast<int64_t>(Hkv) * units_per_head<ROWS>(seq_geom(a, i), group);
+        const int64_t span = static_cast<int64_t>(Hkv) * units_per_head<ROWS, KT>(seq_geom(a, i), group);
         if (u_begin < base + span) {
           s_loc[0] = i;
           s_loc[1] = static_cast<int>(base);
@@ -307,7 +400,7 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
   }
   // Per-lane global element offsets of the tile loads (row kr of the tile,
   // the 16-byte piece that lands in this lane's LDS slot), for K and V.
-  constexpr int kIters = kKeysPerTile * S::kPieces / NT;
+  constexpr int kIters = KT * S::kPieces / NT;
   const int64_t tok_stride = static_cast<int64_t>(Hkv) * D;  // elements between token rows
   int krow[kIters], kgo[kIters], vgo[kIters];
 #pragma unroll
@@ -333,21 +426,31 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
   const uint32_t qflip = a.negate_q ? 0x80008000u : 0u;
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
+  // Split-item pieces this workgroup stores (at most its first and its last
+  // segment), counted at the end.
+  int pend_n[2] = {0, 0};
+  int pend_seq[2] = {0, 0};
+  int pend_h[2] = {0, 0};
+  int pend_qt[2] = {0, 0};
+  int64_t pend_first[2] = {0, 0};
+  int64_t pend_item_first[2] = {0, 0};
+  __shared__ int s_cnt[2];
+
   // ---- 3. Segments.
   int64_t u = u_begin;
   while (u < u_end) {
     const SeqGeom sg = seq_geom(a, seq);
-    const int uph = units_per_head<ROWS>(sg, group);
+    const int uph = units_per_head<ROWS, KT>(sg, group);
     const int64_t r = u - seq_base;
     const int h = static_cast<int>(r / uph);
     int r2 = static_cast<int>(r % uph);
     int qt = 0;
     int acc_units = 0;
-    int nkt = tiles_of<ROWS>(sg, group, 0);
+    int nkt = tiles_of<ROWS, KT>(sg, group, 0);
     while (r2 >= acc_units + nkt) {
       acc_units += nkt;
       ++qt;
-      nkt = tiles_of<ROWS>(sg, group, qt);
+      nkt = tiles_of<ROWS, KT>(sg, group, qt);
     }
     const int t_lo = r2 - acc_units;
     const int64_t item_first = seq_base + static_cast<int64_t>(h) * uph + acc_units;
@@ -356,6 +459,22 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
     const int t_hi = t_lo + static_cast<int>(seg_end - u);
     const int total_keys = sg.c + sg.n;
 
+    // The segment's first K/V tile starts loading before the query rows, so
+    // the two latencies overlap.
+    const int32_t* table = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks_per_seq;
+    const int64_t head_off = static_cast<int64_t>(h) * D;
+    TileSrc<D, NT, KT> src;
+    src.kpool = kpool;
+    src.vpool = vpool;
+    src.kg = kg;
+    src.vg = vg;
+    src.table = table;
+    src.tok_stride = tok_stride;
+    src.head_off = head_off;
+    src.start = sg.start;
+    src.c = sg.c;
+    src.total = total_keys;
+    if (t_lo < t_hi) issue_tile<D, NT, KT>(src, t_lo, s_kv[0], krow, kgo, vgo, tid, wave);
     // This wave's query columns: nt in {0,1}, column col.
     int qrow_tok[2];   // token index j of the lane's query column (may be >= n: padding)
     int qrow_head[2];  // query head
@@ -376,6 +495,11 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
         qf[nt][kc] = __builtin_bit_cast(bf16x8_t, w4);
       }
     }
+    // Later prologue tiles are issued after the query rows, so the wait for
+    // those rows (in-order completion) does not wait for them.
+#pragma unroll
+    for (int i = 1; i < kAhead; ++i)
+      if (t_lo + i < t_hi) issue_tile<D, NT, KT>(src, t_lo + i, s_kv[i], krow, kgo, vgo, tid, wave);
     // Keys a query column may see: positions <= c + j, clamped to the last key.
     int vis[2];
 #pragma unroll
@@ -395,37 +519,40 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
       for (int dt = 0; dt < S::kDTiles; ++dt) acc_o[nt][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    const int32_t* table = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks_per_seq;
-    const int64_t head_off = static_cast<int64_t>(h) * D;
-    TileSrc<D, NT> src;
-    src.kpool = kpool;
-    src.vpool = vpool;
-    src.kg = kg;
-    src.vg = vg;
-    src.table = table;
-    src.tok_stride = tok_stride;
-    src.head_off = head_off;
-    src.start = sg.start;
-    src.c = sg.c;
-    src.total = total_keys;
-    if (t_lo < t_hi) issue_tile<D, NT>(src, t_lo, s_kv[0], krow, kgo, vgo, tid, wave);
     for (int kt = t_lo; kt < t_hi; ++kt) {
-      const int k0 = kt * kKeysPerTile;
-      const int stage = (kt - t_lo) & 1;
-      if (kt + 1 < t_hi) {
-        issue_tile<D, NT>(src, kt + 1, s_kv[stage ^ 1], krow, kgo, vgo, tid, wave);
-        wait_vmcnt<2 * kIters>();  // this tile's loads are done, the next one's may fly
+      const int k0 = kt * KT;
+      const int rel = kt - t_lo;
+      const int stage = rel % kStages;
+      constexpr int L = 2 * kIters;  // loads per tile per thread
+      if constexpr (kAhead >= 2) {
+        // Tiles kt .. kt + kAhead - 1 are in flight: wait for kt, then one
+        // barrier makes tile kt complete for every wave and shows every wave
+        // is done with tile kt - 1, whose stage then takes tile kt + kAhead.
+        const int later = min(kAhead - 1, t_hi - 1 - kt);  // tiles after kt in flight
+        if (later >= 2 && kAhead >= 3) wait_vmcnt<(kAhead >= 3 ? 2 : 0) * L>();
+        else if (later >= 1) wait_vmcnt<L>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (kt + kAhead < t_hi)
+          issue_tile<D, NT, KT>(src, kt + kAhead, s_kv[(rel + kAhead) % kStages], krow, kgo, vgo, tid, wave);
       } else {
-        wait_vmcnt<0>();
+        // Issue tile kt + 1 into the other stage (every wave finished with it
+        // at the barrier ending the previous tile), then wait for tile kt.
+        if (kt + 1 < t_hi) {
+          issue_tile<D, NT, KT>(src, kt + 1, s_kv[(rel + 1) % kStages], krow, kgo, vgo, tid, wave);
+          wait_vmcnt<L>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        __syncthreads();
       }
-      __syncthreads();
       const char* s_k = s_kv[stage];
       const char* s_v = s_kv[stage] + TB;
 
       // -- S^T = K Q^T: st[mt][nt] holds keys 16mt + 4grp + e of query column col
-      f32x4_t st[4][2];
+      f32x4_t st[S::kMt][2];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < S::kMt; ++mt) {
         st[mt][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         st[mt][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -437,12 +564,12 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
       }
 
       // -- online softmax per query column (raw scores; sc > 0)
-      const bool full_tile = k0 + kKeysPerTile - 1 <= wave_min_vis;
+      const bool full_tile = k0 + KT - 1 <= wave_min_vis;
       if (!full_tile) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
+          for (int mt = 0; mt < S::kMt; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               if (k0 + mt * 16 + grp * 4 + e > vis[nt]) st[mt][nt][e] = -INFINITY;
@@ -453,7 +580,7 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
       for (int nt = 0; nt < 2; ++nt) {
         float t = fmaxf(fmaxf(st[0][nt][0], st[0][nt][1]), fmaxf(st[0][nt][2], st[0][nt][3]));
 #pragma unroll
-        for (int mt = 1; mt < 4; ++mt)
+        for (int mt = 1; mt < S::kMt; ++mt)
           t = fmaxf(t, fmaxf(fmaxf(st[mt][nt][0], st[mt][nt][1]), fmaxf(st[mt][nt][2], st[mt][nt][3])));
         t = fmaxf(t, shfl_xor_f32(t, 16));
         t = fmaxf(t, shfl_xor_f32(t, 32));
@@ -472,12 +599,12 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
       }
       // P^T operands, bf16: for key step kc2 the lane's 8 keys are
       // {4grp..4grp+3} of S^T tile 2kc2 and the same of tile 2kc2+1.
-      bf16x8_t pb[2][2];
+      bf16x8_t pb[2][S::kKc2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const float nm = -m[nt];
 #pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2) {
+        for (int kc2 = 0; kc2 < S::kKc2; ++kc2) {
           const f32x4_t& s0 = st[2 * kc2][nt];
           const f32x4_t& s1 = st[2 * kc2 + 1][nt];
           const u32x4_t w = {pack_bf16x2(exp2_fast(fmaf(s0[0], sc, nm)), exp2_fast(fmaf(s0[1], sc, nm))),
@@ -490,7 +617,7 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
 
       // -- O^T += V^T P^T, and the row sums from the same bf16 P
 #pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2) {
+      for (int kc2 = 0; kc2 < S::kKc2; ++kc2) {
 #pragma unroll
         for (int dt = 0; dt < S::kDTiles; ++dt) {
           const char* pv = s_v + voff[dt] + kc2 * 32 * RB;
@@ -505,7 +632,7 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
         lsum[0] = mfma16(ones, pb[0][kc2], lsum[0]);
         lsum[1] = mfma16(ones, pb[1][kc2], lsum[1]);
       }
-      __syncthreads();  // the next tile overwrites the LDS tiles
+      if constexpr (kAhead < 2) __syncthreads();  // the next tile overwrites the other stage
     }
 
     // ---- finish the segment: output or partial
@@ -546,75 +673,15 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
           store4_agent(pr, (row * D + dt * 16 + grp * 4) * 4, acc_o[nt][dt] * inv);
         if (grp == 0) store_agent(a.part_lse + slot * ROWS + row, seen ? m[nt] + __log2f(lt[nt]) : -INFINITY);
       }
-      wait_vector_memory();
-      __syncthreads();
-      if (tid == 0) {
-        const int64_t qtiles_max = (static_cast<int64_t>(a.max_q_len) * group + ROWS - 1) / ROWS;
-        int* ctr = a.counters + (static_cast<int64_t>(seq) * Hkv + h) * qtiles_max + qt;
-        const int prev = add_agent(ctr, 1);
-        const int last = prev == n_parts - 1;
-        if (last) store_agent_int(ctr, 0);
-        s_last = last;
-      }
-      __syncthreads();
-      if (s_last) {
-        // Merge the pieces in order. Piece p is owned by workgroup
-        // first_owner + p; it is that workgroup's first segment except for
-        // the first piece when its owner started inside an earlier item.
-        // Each thread owns 4 consecutive dims of kMergeRows rows at a time
-        // and issues all of a piece's loads together.
-        const int64_t first_start = static_cast<int64_t>(first_owner) * U / G;
-        constexpr int D4 = D / 4;
-        constexpr int kRowStep = NT / D4;
-        constexpr int kMergeRows = 8;
-        const int d4 = tid % D4;
-        for (int rb = tid / D4; rb < ROWS; rb += kRowStep * kMergeRows) {
-          float mxr[kMergeRows];
-#pragma unroll
-          for (int k = 0; k < kMergeRows; ++k) mxr[k] = -INFINITY;
-          for (int p = 0; p < n_parts; ++p) {
-            const int64_t sl = 2 * static_cast<int64_t>(first_owner + p) + ((p == 0 && first_start < item_first) ? 1 : 0);
-#pragma unroll
-            for (int k = 0; k < kMergeRows; ++k) {
-              const int row = rb + k * kRowStep;
-              if (row < ROWS) mxr[k] = fmaxf(mxr[k], load_agent(a.part_lse + sl * ROWS + row));
-            }
-          }
-          f32x4_t num[kMergeRows];
-          float den[kMergeRows];
-#pragma unroll
-          for (int k = 0; k < kMergeRows; ++k) {
-            num[k] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            den[k] = 0.0f;
-          }
-          for (int p = 0; p < n_parts; ++p) {
-            const int64_t sl = 2 * static_cast<int64_t>(first_owner + p) + ((p == 0 && first_start < item_first) ? 1 : 0);
-            const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(a.part_out + sl * ROWS * D, ROWS * D * 4);
-#pragma unroll
-            for (int k = 0; k < kMergeRows; ++k) {
-              const int row = rb + k * kRowStep;
-              if (row >= ROWS) continue;
-              const float f = exp2_fast(load_agent(a.part_lse + sl * ROWS + row) - mxr[k]);
-              const f32x4_t o4 = load4_agent(pr, (row * D + 4 * d4) * 4);
-              num[k] += f * o4;
-              den[k] += f;
-            }
-          }
-#pragma unroll
-          for (int k = 0; k < kMergeRows; ++k) {
-            const int row = rb + k * kRowStep;
-            if (row >= ROWS) continue;
-            const int R = qt * ROWS + row;
-            const int j = R / group;
-            if (j >= sg.n) continue;
-            const float inv = 1.0f / den[k];
-            const uint32_t lo = pack_bf16x2(num[k][0] * inv, num[k][1] * inv);
-            const uint32_t hi = pack_bf16x2(num[k][2] * inv, num[k][3] * inv);
-            bf16_t* orow = outp + (static_cast<int64_t>(sg.start + j) * a.num_q_heads + h * group + R % group) * D;
-            *reinterpret_cast<uint2*>(orow + 4 * d4) = make_uint2(lo, hi);
-          }
-        }
-      }
+      // Nothing waits for these stores here: the piece is counted when the
+      // workgroup ends. Only a range's first and last segment can be pieces.
+      const int k = pend_n[0] == 0 ? 0 : 1;
+      pend_n[k] = n_parts;
+      pend_first[k] = first_owner;
+      pend_item_first[k] = item_first;
+      pend_seq[k] = seq;
+      pend_h[k] = h;
+      pend_qt[k] = qt;
     }
     __syncthreads();
 
@@ -624,25 +691,57 @@ __global__ __launch_bounds__(64 * WM, 2) void paged_prefill_kernel(PrefillArgs a
       if (u - seq_base >= static_cast<int64_t>(Hkv) * uph) {
         seq_base = u;
         ++seq;
-        while (seq < B - 1 && units_per_head<ROWS>(seq_geom(a, seq), group) == 0) ++seq;
+        while (seq < B - 1 && units_per_head<ROWS, KT>(seq_geom(a, seq), group) == 0) ++seq;
+      }
+    }
+  }
+
+  // ---- 4. Count the stored pieces once every thread's stores are complete;
+  // the workgroup whose count completes an item merges its pieces.
+  if (pend_n[0] > 0) {
+    wait_vector_memory();
+    __syncthreads();
+    const int64_t qtiles_max = (static_cast<int64_t>(a.max_q_len) * group + ROWS - 1) / ROWS;
+    if (tid < 2) {  // threads 0 and 1 count the two pieces
+      const int n = tid == 0 ? pend_n[0] : pend_n[1];
+      int last = 0;
+      if (n > 0) {
+        const int64_t item = static_cast<int64_t>(tid == 0 ? pend_seq[0] : pend_seq[1]) * Hkv +
+                             (tid == 0 ? pend_h[0] : pend_h[1]);
+        int* ctr = a.counters + item * qtiles_max + (tid == 0 ? pend_qt[0] : pend_qt[1]);
+        last = add_agent(ctr, 1) == n - 1;
+        if (last) store_agent_int(ctr, 0);
+      }
+      s_cnt[tid] = last;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (pend_n[k] > 0 && s_cnt[k]) {
+        const bool late = pend_first[k] * U / G < pend_item_first[k];
+        merge_pieces<D, ROWS, NT>(a, outp, pend_first[k], pend_n[k], late, seq_geom(a, pend_seq[k]), pend_qt[k],
+                                  pend_h[k], group, tid);
       }
     }
   }
 }
 
-template <int D, int WM>
+template <int D, int WM, int KT>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
-  paged_prefill_kernel<D, WM><<<dim3(static_cast<uint32_t>(a.num_workgroups)), dim3(64 * WM), 0, stream>>>(a);
+  paged_prefill_kernel<D, WM, KT><<<dim3(static_cast<uint32_t>(a.num_workgroups)), dim3(64 * WM), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, int32_t head_dim, hipStream_t stream) {
-  if (a.rows_per_tile == 128) {
-    return head_dim == 128 ? launch_typed<128, 4>(a, stream) : launch_typed<64, 4>(a, stream);
+  if (a.rows_per_tile == 256) {
+    return head_dim == 128 ? launch_typed<128, 8, 64>(a, stream) : launch_typed<64, 8, 64>(a, stream);
   }
-  return head_dim == 128 ? launch_typed<128, 1>(a, stream) : launch_typed<64, 1>(a, stream);
+  if (a.rows_per_tile == 128) {
+    return head_dim == 128 ? launch_typed<128, 4, 64>(a, stream) : launch_typed<64, 4, 64>(a, stream);
+  }
+  return head_dim == 128 ? launch_typed<128, 1, 64>(a, stream) : launch_typed<64, 1, 64>(a, stream);
 }
 
 }  // namespace pa
