@@ -124,12 +124,19 @@ __device__ __forceinline__ int qtiles_of(const SeqGeom& s, int group) {
   return (s.n * group + ROWS - 1) / ROWS;
 }
 
+// An item (sequence, KV head, query tile) costs its key tiles plus
+// kItemCost units ahead of them that hold no tiles: they stand for the fixed
+// work of a segment (loading its query rows, the first tile's latency, the
+// output and the barriers), about three tiles' time on MI355X, so ranges of
+// many items carry fewer tiles and all ranges take about the same time.
+constexpr int kItemCost = 3;
+
 template <int ROWS, int KT>
 __device__ int units_per_head(const SeqGeom& s, int group) {
   if (s.n <= 0) return 0;
   const int qts = qtiles_of<ROWS>(s, group);
   int u = 0;
-  for (int qt = 0; qt < qts; ++qt) u += tiles_of<ROWS, KT>(s, group, qt);
+  for (int qt = 0; qt < qts; ++qt) u += tiles_of<ROWS, KT>(s, group, qt) + kItemCost;
   return u;
 }
 
@@ -437,6 +444,7 @@ __global__ __launch_bounds__(64 * WM, WM >= 8 ? 1 : 2) void paged_prefill_kernel
   __shared__ int s_cnt[2];
 
   // ---- 3. Segments.
+  bool first_seg = true;  // no segment with tiles done yet (its piece goes to slot 2w)
   int64_t u = u_begin;
   while (u < u_end) {
     const SeqGeom sg = seq_geom(a, seq);
@@ -447,16 +455,28 @@ __global__ __launch_bounds__(64 * WM, WM >= 8 ? 1 : 2) void paged_prefill_kernel
     int qt = 0;
     int acc_units = 0;
     int nkt = tiles_of<ROWS, KT>(sg, group, 0);
-    while (r2 >= acc_units + nkt) {
-      acc_units += nkt;
+    while (r2 >= acc_units + nkt + kItemCost) {
+      acc_units += nkt + kItemCost;
       ++qt;
       nkt = tiles_of<ROWS, KT>(sg, group, qt);
     }
-    const int t_lo = r2 - acc_units;
+    // cost units of the item: kItemCost virtual ones, then one per key tile
     const int64_t item_first = seq_base + static_cast<int64_t>(h) * uph + acc_units;
-    const int64_t item_end = item_first + nkt;
+    const int64_t real_first = item_first + kItemCost;
+    const int64_t item_end = real_first + nkt;
     const int64_t seg_end = u_end < item_end ? u_end : item_end;
-    const int t_hi = t_lo + static_cast<int>(seg_end - u);
+    const int64_t lo = u > real_first ? u : real_first;
+    if (lo >= seg_end) {  // only virtual units of this item lie in the range
+      u = seg_end;
+      if (u == item_end && u < u_end && u - seq_base >= static_cast<int64_t>(Hkv) * uph) {
+        seq_base = u;
+        ++seq;
+        while (seq < B - 1 && units_per_head<ROWS, KT>(seq_geom(a, seq), group) == 0) ++seq;
+      }
+      continue;
+    }
+    const int t_lo = static_cast<int>(lo - real_first);
+    const int t_hi = static_cast<int>(seg_end - real_first);
     const int total_keys = sg.c + sg.n;
 
     // The segment's first K/V tile starts loading before the query rows, so
@@ -639,7 +659,7 @@ __global__ __launch_bounds__(64 * WM, WM >= 8 ? 1 : 2) void paged_prefill_kernel
     float lt[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) lt[nt] = lsum[nt][0];
-    const int first_owner = owner_of_unit(item_first, U, G);
+    const int first_owner = owner_of_unit(real_first, U, G);
     const int n_parts = owner_of_unit(item_end - 1, U, G) - first_owner + 1;
     if (n_parts == 1) {
 #pragma unroll
@@ -655,12 +675,12 @@ __global__ __launch_bounds__(64 * WM, WM >= 8 ? 1 : 2) void paged_prefill_kernel
         }
       }
     } else {
-      // Partial slot of this piece: a workgroup's first segment uses slot
-      // 2w, its last (when it has more than one) uses slot 2w + 1.
+      // Partial slot of this piece: a workgroup's first segment with tiles
+      // uses slot 2w, its last (when it has more than one) uses slot 2w + 1.
       // A piece may hold only keys that are causally hidden from some of its
       // rows (sum 0): such a row's partial is 0 with log-sum-exp -inf, so the
       // merge gives it weight 0.
-      const int which = u > u_begin ? 1 : 0;
+      const int which = first_seg ? 0 : 1;
       const int64_t slot = 2 * static_cast<int64_t>(w) + which;
       const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(a.part_out + slot * ROWS * D, ROWS * D * 4);
 #pragma unroll
@@ -684,6 +704,7 @@ __global__ __launch_bounds__(64 * WM, WM >= 8 ? 1 : 2) void paged_prefill_kernel
       pend_qt[k] = qt;
     }
     __syncthreads();
+    first_seg = false;
 
     u = seg_end;
     if (u == item_end && u < u_end) {
