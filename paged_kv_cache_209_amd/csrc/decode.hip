@@ -312,12 +312,13 @@ struct SegmentWalk {
   EvenSplit split;
   int64_t u, u_end, seq_base;
   int seq, B, HG, max_ctx;
+  int known_seq, known_ctx;  // one length already read (the first sequence's)
   const int32_t* context_lens;
 
   // The next segment with tokens, if any is left in the range.
   __device__ __forceinline__ bool next(Segment& s) {
     while (u < u_end) {
-      const int ctx_raw = load_uniform(context_lens, seq);
+      const int ctx_raw = seq == known_seq ? known_ctx : load_uniform(context_lens, seq);
       const int nu = context_units(ctx_raw, max_ctx);
       const int ctx = min(ctx_raw, max_ctx);
       const int64_t span = nu + kItemCost;  // cost units of one item of this sequence
@@ -430,8 +431,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
   constexpr int kStride = kDecodeWaves * kChunk;  // tokens between a wave's chunks
   constexpr int kQVecs = GT * D * Elem<T>::kBytes / 16;  // 16-byte pieces of a group's query rows
   constexpr int kQPerLane = (kQVecs + kWave - 1) / kWave;
-  __shared__ int s_scan[kDecodeThreads];
-  __shared__ int s_loc[2];
+  __shared__ int s_wsum[kDecodeWaves];
+  __shared__ int s_loc[3];
   __shared__ float s_acc[kDecodeWaves][GT][D];
   __shared__ float s_m[kDecodeWaves][GT];
   __shared__ float s_l[kDecodeWaves][GT];
@@ -450,24 +451,33 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
   const int group = a.num_q_heads / a.num_kv_heads;
   const int groups_per_kv = group / GT;
 
-  // ---- 1. Work units: item (seq i, head group hg) has ceil(ctx_i / 256)
-  // units of one 256-token block each, ordered seq-major. Count them with a
-  // block-wide scan over the sequences.
+  // ---- 1. Cost units: item (seq i, head group hg) costs one unit per 64
+  // context tokens plus kItemCost units of fixed work, ordered seq-major.
+  // Count them with a workgroup-wide scan over the sequences.
   const int per = (B + kDecodeThreads - 1) / kDecodeThreads;
   int mine = 0;
   for (int k = 0; k < per; ++k) {
     const int i = tid * per + k;
     if (i < B) mine += item_cost(a.context_lens[i], a.max_context_len);
   }
-  s_scan[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < kDecodeThreads; off <<= 1) {
-    const int v = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
+  // Inclusive prefix sum of `mine` over the workgroup: within each wave by
+  // lane shuffles, then across the waves through LDS (one barrier).
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += t;
   }
-  const int64_t U = static_cast<int64_t>(HG) * __builtin_amdgcn_readfirstlane(s_scan[kDecodeThreads - 1]);
+  if (lane == kWave - 1) s_wsum[wave] = incl;
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int k = 0; k < kDecodeWaves; ++k) {
+    const int v = s_wsum[k];
+    if (k < wave) incl += v;
+    total += v;
+  }
+  const int64_t U = static_cast<int64_t>(HG) * total;
   // With no more workgroups than units every workgroup owns at least one
   // unit, so the owners of an item's units are consecutive workgroups, and
   // only the first and the last segment of a range can be pieces of items
@@ -482,8 +492,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
   // ---- 2. The sequence holding u_begin: the thread whose sequences span it
   // walks them.
   {
-    const int64_t lo = static_cast<int64_t>(HG) * (s_scan[tid] - mine);
-    const int64_t hi = static_cast<int64_t>(HG) * s_scan[tid];
+    const int64_t lo = static_cast<int64_t>(HG) * (incl - mine);
+    const int64_t hi = static_cast<int64_t>(HG) * incl;
     if (u_begin >= lo && u_begin < hi) {
       int64_t base = lo;
       for (int k = 0; k < per && tid * per + k < B; ++k) {
@@ -491,7 +501,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
         const int64_t span = static_cast<int64_t>(HG) * item_cost(a.context_lens[i], a.max_context_len);
         if (u_begin < base + span) {
           s_loc[0] = i;
-          s_loc[1] = static_cast<int>(base / HG);  // blocks of all earlier sequences
+          s_loc[1] = static_cast<int>(base / HG);  // cost units of all earlier sequences
+          s_loc[2] = a.context_lens[i];            // its length, so the walk need not read it again
           break;
         }
         base += span;
@@ -506,6 +517,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
   // scalar registers
   walk.seq_base = static_cast<int64_t>(HG) * __builtin_amdgcn_readfirstlane(s_loc[1]);
   walk.seq = __builtin_amdgcn_readfirstlane(s_loc[0]);
+  walk.known_seq = walk.seq;
+  walk.known_ctx = __builtin_amdgcn_readfirstlane(s_loc[2]);
   walk.split = split;
   walk.B = B;
   walk.HG = HG;
