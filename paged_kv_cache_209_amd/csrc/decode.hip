@@ -5,11 +5,12 @@
 // rows are streamed from the pool in place and never copied.
 //
 // Work split. An item is (sequence, group of GT query heads sharing one KV
-// head); it has one work unit per 256-token block of its context. The units of
-// all items, ordered sequence-major, are cut into equal contiguous ranges, one
-// per workgroup, so every workgroup streams the same number of blocks however
-// ragged the contexts are. A range may hold the tail of one item, whole items
-// and the head of another; each such piece is a segment.
+// head); it costs one unit per 64 tokens of its context plus a fixed cost for
+// finishing it. The units of all items, ordered sequence-major, are cut into
+// equal contiguous ranges, one per workgroup, so every workgroup has about
+// the same time of work however ragged the contexts are. A range may hold the
+// tail of one item, whole items and the head of another; each such piece is a
+// segment.
 //
 // Data flow inside a workgroup (256 threads = 4 wave64, gfx950):
 //   * the 4 waves take 16-token chunks of a segment round-robin, each wave
@@ -27,9 +28,10 @@
 //     rescale off the common path without risking overflow;
 //   * p.V pairs two tokens per v_dot2_f32_bf16 (p rounded to bf16, and l
 //     accumulated from the same rounded p so the weights stay normalised);
-//   * at the end of a segment the 8 groups of a wave merge by lane shuffles,
-//     the 4 waves through LDS; a whole item is written as the final output,
-//     a piece as a (normalised output, log2-sum-exp) partial.
+//   * at the end of a segment the 8 groups of a wave merge by VALU lane
+//     swaps and a row rotate (no LDS traffic), the 4 waves through LDS; a
+//     whole item is written as the final output, a piece as a (normalised
+//     output, log2-sum-exp) partial.
 //   * consecutive segments overlap: the next segment's block-table window,
 //     query rows and first chunk load while the current one finishes;
 //   * the pieces of a split item are counted on a device-scope counter per
@@ -306,25 +308,38 @@ struct Segment {
   int64_t item_first;    // the item's first cost unit (a virtual one)
 };
 
-// Walks the segments of the unit range [u, u_end) in order. All its state is
+// Walks the segments of the unit range [u, u_end) in order, item by item:
+// after the first item the walk only steps forward, so it divides only for
+// the owners of items that cross the range's ends. All its state is
 // wave-uniform (kept in scalar registers).
 struct SegmentWalk {
   EvenSplit split;
-  int64_t u, u_end, seq_base;
-  int seq, B, HG, max_ctx;
-  int known_seq, known_ctx;  // one length already read (the first sequence's)
+  int64_t u, u_end;    // units still to walk
+  int64_t range_lo;    // first unit of the workgroup's range
+  int64_t item_first;  // first cost unit of the current item (a virtual one)
+  int w;               // the workgroup (owner of the range)
+  int seq, hg;         // the current item
+  int ctx;             // its sequence's length as given
+  int B, HG, max_ctx;
   const int32_t* context_lens;
+
+  // Places the walk at unit u0 of sequence seq0, whose units start at
+  // seq_base and whose length is ctx0.
+  __device__ __forceinline__ void start(int64_t u0, int64_t u1, int seq0, int64_t seq_base, int ctx0) {
+    u = u0;
+    u_end = u1;
+    range_lo = u0;
+    seq = seq0;
+    ctx = ctx0;
+    const int64_t span = context_units(ctx0, max_ctx) + kItemCost;
+    hg = static_cast<int>((u0 - seq_base) / span);
+    item_first = seq_base + hg * span;
+  }
 
   // The next segment with tokens, if any is left in the range.
   __device__ __forceinline__ bool next(Segment& s) {
     while (u < u_end) {
-      const int ctx_raw = seq == known_seq ? known_ctx : load_uniform(context_lens, seq);
-      const int nu = context_units(ctx_raw, max_ctx);
-      const int ctx = min(ctx_raw, max_ctx);
-      const int64_t span = nu + kItemCost;  // cost units of one item of this sequence
-      const int64_t r = u - seq_base;
-      const int hg = static_cast<int>(r / span);
-      const int64_t item_first = seq_base + hg * span;
+      const int64_t span = context_units(ctx, max_ctx) + kItemCost;  // cost units of the item
       const int64_t real_first = item_first + kItemCost;
       const int64_t item_end = item_first + span;
       const int64_t seg_end = u_end < item_end ? u_end : item_end;
@@ -334,18 +349,28 @@ struct SegmentWalk {
         s.seq = seq;
         s.hg = hg;
         s.t_lo = static_cast<int>(lo - real_first) * kDecodeUnitTokens;
-        s.t_hi = min(ctx, static_cast<int>(seg_end - real_first) * kDecodeUnitTokens);
+        s.t_hi = min(min(ctx, max_ctx), static_cast<int>(seg_end - real_first) * kDecodeUnitTokens);
         s.b_lo = s.t_lo / kTokensPerBlock;
         s.b_hi = (s.t_hi + kTokensPerBlock - 1) / kTokensPerBlock;
-        s.first_owner = split.owner(real_first);
-        s.n_parts = static_cast<int>(split.owner(item_end - 1) - s.first_owner + 1);
+        // lo < seg_end <= u_end: the item's real units start before the
+        // range ends, and in it unless they start before it
+        s.first_owner = real_first >= range_lo ? w : split.owner(real_first);
+        const int64_t last_owner = item_end <= u_end ? w : split.owner(item_end - 1);
+        s.n_parts = static_cast<int>(last_owner - s.first_owner + 1);
         s.item_first = item_first;
       }
       u = seg_end;
-      if (u == item_end && hg == HG - 1) {  // next sequence with work
-        seq_base = item_end;
-        ++seq;
-        while (u < u_end && seq < B - 1 && context_units(load_uniform(context_lens, seq), max_ctx) == 0) ++seq;
+      if (u == item_end) {  // on to the next item
+        item_first = item_end;
+        if (++hg == HG) {  // ... of the next sequence with work (an empty one has no units)
+          hg = 0;
+          ++seq;
+          if (u < u_end) {
+            int c = load_uniform(context_lens, seq);
+            while (context_units(c, max_ctx) == 0 && seq < B - 1) c = load_uniform(context_lens, ++seq);
+            ctx = c;
+          }
+        }
       }
       if (has_tokens) return true;
     }
@@ -511,19 +536,17 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
   }
   __syncthreads();
   SegmentWalk walk;
-  walk.u = u_begin;
-  walk.u_end = u_end;
-  // values read back from LDS are uniform; say so, so that the walk stays in
-  // scalar registers
-  walk.seq_base = static_cast<int64_t>(HG) * __builtin_amdgcn_readfirstlane(s_loc[1]);
-  walk.seq = __builtin_amdgcn_readfirstlane(s_loc[0]);
-  walk.known_seq = walk.seq;
-  walk.known_ctx = __builtin_amdgcn_readfirstlane(s_loc[2]);
   walk.split = split;
+  walk.w = w;
   walk.B = B;
   walk.HG = HG;
   walk.max_ctx = a.max_context_len;
   walk.context_lens = a.context_lens;
+  // values read back from LDS are uniform; say so, so that the walk stays in
+  // scalar registers
+  walk.start(u_begin, u_end, __builtin_amdgcn_readfirstlane(s_loc[0]),
+             static_cast<int64_t>(HG) * __builtin_amdgcn_readfirstlane(s_loc[1]),
+             __builtin_amdgcn_readfirstlane(s_loc[2]));
 
   const int64_t row_stride = static_cast<int64_t>(a.num_kv_heads) * D;
   const float sc = a.scale_log2;
@@ -644,22 +667,36 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
     load_chunk<T, D>(cur, n_kpool, n_vpool, bwn.get(n_c0 / kTokensPerBlock, lane), row_stride, n_c0, ns.t_hi, ts, sl);
     consume_chunk<T, D, GT>(st, nxt, sq, sl, two && c0 + ts < t_end, two && c0 + 8 + ts < t_end, sc);
 
-    // Merge the 8 lane groups of each wave (lane distance 8, 16, 32) ...
+    // Merge the 8 lane groups of each wave into lanes 0-7: the upper half
+    // into the lower, odd rows into even ones (VALU lane swaps that hand
+    // every lane both values), then lanes 8-15 into 0-7 (row rotate by 8) ...
 #pragma unroll
-    for (int step = 0; step < 3; ++step) {
-      const int mask = 8 << step;
+    for (int g = 0; g < GT; ++g) {
 #pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        const float mo = shfl_xor_f32(st.m[g], mask);
-        const float lo = shfl_xor_f32(st.l[g], mask);
-        const float mx = fmaxf(st.m[g], mo);
-        const float fa = exp2_fast(st.m[g] - mx);
-        const float fb = exp2_fast(mo - mx);
-        st.l[g] = st.l[g] * fa + lo * fb;
+      for (int step = 0; step < 2; ++step) {
+        const auto pair = [step](float x) { return step == 0 ? pair_across_halves(x) : pair_across_rows(x); };
+        const LanePair pm = pair(st.m[g]);
+        const LanePair pl = pair(st.l[g]);
+        const float mx = fmaxf(pm.lo, pm.hi);
+        const float fa = exp2_fast(pm.lo - mx);
+        const float fb = exp2_fast(pm.hi - mx);
+        st.l[g] = pl.lo * fa + pl.hi * fb;
 #pragma unroll
-        for (int j = 0; j < E; ++j) st.acc[g][j] = st.acc[g][j] * fa + shfl_xor_f32(st.acc[g][j], mask) * fb;
+        for (int j = 0; j < E; ++j) {
+          const LanePair pa = pair(st.acc[g][j]);
+          st.acc[g][j] = pa.lo * fa + pa.hi * fb;
+        }
         st.m[g] = mx;
       }
+      const float mo = dpp_f32<kDppRowRor8>(st.m[g]);
+      const float lo = dpp_f32<kDppRowRor8>(st.l[g]);
+      const float mx = fmaxf(st.m[g], mo);
+      const float fa = exp2_fast(st.m[g] - mx);
+      const float fb = exp2_fast(mo - mx);
+      st.l[g] = st.l[g] * fa + lo * fb;
+#pragma unroll
+      for (int j = 0; j < E; ++j) st.acc[g][j] = st.acc[g][j] * fa + dpp_f32<kDppRowRor8>(st.acc[g][j]) * fb;
+      st.m[g] = mx;
     }
     // ... then the 4 waves through LDS.
     if (ts == 0) {

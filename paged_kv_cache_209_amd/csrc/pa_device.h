@@ -87,6 +87,23 @@ __device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
   return __shfl_xor(x, mask, kWave);
 }
 
+// The two values of x at lane positions that differ only in lane bit 5
+// (halves) or bit 4 (16-lane rows), handed to every lane by one VALU swap
+// (v_permlane32_swap / v_permlane16_swap, new in gfx950) instead of an LDS
+// crossbar permute: `lo` is x at the position with the bit clear, `hi` with
+// it set.
+struct LanePair {
+  float lo, hi;
+};
+__device__ __forceinline__ LanePair pair_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair pair_across_rows(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 // A read-only int32 read at a wave-uniform index, through the constant
 // address space, so that it is a scalar load: it waits on the scalar-memory
 // counter, never on the queue of vector loads in flight. Only for arrays that

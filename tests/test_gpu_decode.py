@@ -216,3 +216,32 @@ def test_workspace_reused_across_sizes():
                              workspace_tensor=ws)
         torch.cuda.synchronize()
         compare(out, ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("workgroups", [0, 16, 64, 300])
+def test_repeated_calls_one_workspace(workgroups):
+    """Long contexts over several grids, calls in a row on one workspace: the
+    results are bit-identical from call to call (the pieces of a split item
+    are fixed by the sizes and merged in piece order) and every call leaves
+    the piece counters at zero for the next (a stale count would merge too
+    early or never)."""
+    say("decode repeated calls", workgroups)
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.integers(2000, 6000, size=24)]
+    c = ragged_case(31, lengths, 16, 8, 128, torch.bfloat16)
+    ref = oracle.paged_attn_decode(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.scale)
+    ws = torch.zeros(pa.decode_workspace_bytes(c.num_seqs, c.num_q_heads, c.head_dim, c.max_context_len),
+                     dtype=torch.uint8, device=DEV)
+    q, kc, vc = to_dev(c.q), to_dev(c.k_cache), to_dev(c.v_cache)
+    bt, cl = to_dev(c.block_tables), to_dev(c.context_lens)
+    first = None
+    for _ in range(5):
+        out = torch.empty_like(q)
+        pa.paged_attn_decode(out, q, kc, vc, bt, cl, c.scale, c.max_context_len, num_workgroups=workgroups,
+                             workspace_tensor=ws)
+        torch.cuda.synchronize()
+        if first is None:
+            first = out.cpu()
+            compare(out, ref, torch.bfloat16)
+        else:
+            assert torch.equal(bits(first), bits(out.cpu()))
