@@ -212,7 +212,7 @@ pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const v
   const int64_t seq_rows = static_cast<int64_t>(max_q_len) * group;
   const int32_t rows = seq_rows <= 32 ? 32 : (seq_rows <= 128 ? 128 : 256);
   const int64_t qtiles = ceil_div(seq_rows, rows);
-  const int64_t key_tile = 64;  // keys per work unit (the kernels' tile width)
+  const int64_t key_tile = rows == 32 ? 32 : 64;  // keys per work unit (the kernels' tile width)
   const int64_t max_units = static_cast<int64_t>(num_seqs) * num_kv_heads * qtiles * ceil_div(max_context_len, key_tile);
   const int64_t cap = rows == 256 ? pa::kPrefillMaxWorkgroups256
                                   : (rows == 128 ? pa::kPrefillMaxWorkgroups128 : pa::kPrefillMaxWorkgroups32);

@@ -12,12 +12,12 @@
 // Items and work split. Query rows are (new token j, query head g) pairs of
 // one KV head, token-major, so all GQA heads sharing the KV head ride in one
 // tile. An item is (sequence, KV head, tile of ROWS query rows); its work
-// units are the 64-key tiles its rows can see (causal: up to the tile's last
-// token). As in decode, the units of all items are cut into equal contiguous
+// units are the key tiles (64 keys; 32 for 1-wave tiles) its rows can see
+// (causal: up to the tile's last token). As in decode, the units of all items are cut into equal contiguous
 // shares, one per workgroup; a piece of an item is finished by the last
 // workgroup to reach it, which merges the pieces' partial results in order.
 //
-// Per 64-key tile, each wave (32 query rows = two 16-column MFMA tiles):
+// Per key tile, each wave (32 query rows = two 16-column MFMA tiles):
 //   S^T = K Q^T   with v_mfma_f32_16x16x32_bf16: A = K rows from LDS
 //                 (16 keys x 32 dims per lane group), B = the wave's query
 //                 fragments held in registers. Each lane ends with 4 keys of
@@ -50,8 +50,8 @@ constexpr int kNonTemporal = 2;  // cache-policy operand of direct-to-LDS loads:
 
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-// Shapes for head dim D and key tiles of KT keys (64 on every path here; 32 is
-// supported for experiments with deeper LDS pipelines in the same LDS).
+// Shapes for head dim D and key tiles of KT keys (64 for the 8- and 4-wave
+// tiles, 32 for the 1-wave verify tiles).
 template <int D, int KT>
 struct PShape {
   static constexpr int kDChunks = D / 32;  // k-steps of the Q.K product
@@ -312,17 +312,23 @@ __device__ __forceinline__ void merge_pieces(const PrefillArgs& a, bf16_t* outp,
 }
 
 // LDS stages of [K tile | V tile] per workgroup: the 8-wave workgroup (one
-// per CU) keeps two tiles in flight while it works on a third; the smaller
-// ones (two per CU) keep one. (Three stages of 32-key tiles for the 1-wave
-// verify workgroup, in the same LDS, measured 25% slower on MI355X: the fixed
-// cost per tile outweighs the extra loads in flight.)
+// per CU) keeps two 64-key tiles in flight while it works on a third; the
+// 4-wave ones (two per CU) keep one. The 1-wave verify workgroup takes
+// 32-key tiles, two stages (32 KB), so that four fit in a CU's LDS: measured
+// on MI355X, four such workgroups per CU stream 8% faster than two with
+// 64-key tiles (more waves, and more loads in flight per CU), while one or
+// two workgroups with deeper pipelines are slower.
 template <int WM>
 constexpr int prefill_stages() {
   return WM >= 8 ? 3 : 2;
 }
+template <int WM>
+constexpr int prefill_workgroups_per_cu() {
+  return WM >= 8 ? 1 : (WM == 1 ? 4 : 2);
+}
 
 template <int D, int WM, int KT>
-__global__ __launch_bounds__(64 * WM, WM >= 8 ? 1 : 2) void paged_prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * WM, prefill_workgroups_per_cu<WM>()) void paged_prefill_kernel(PrefillArgs a) {
   using S = PShape<D, KT>;
   constexpr int ROWS = kRowsPerWave * WM;
   constexpr int NT = kWave * WM;
@@ -602,8 +608,12 @@ __global__ __launch_bounds__(64 * WM, WM >= 8 ? 1 : 2) void paged_prefill_kernel
 #pragma unroll
         for (int mt = 1; mt < S::kMt; ++mt)
           t = fmaxf(t, fmaxf(fmaxf(st[mt][nt][0], st[mt][nt][1]), fmaxf(st[mt][nt][2], st[mt][nt][3])));
-        t = fmaxf(t, shfl_xor_f32(t, 16));
-        t = fmaxf(t, shfl_xor_f32(t, 32));
+        {
+          const LanePair r = pair_across_rows(t);
+          t = fmaxf(r.lo, r.hi);
+          const LanePair h = pair_across_halves(t);
+          t = fmaxf(h.lo, h.hi);
+        }
         mx[nt] = fmaxf(m[nt], t * sc);
         need |= mx[nt] > m[nt] + kSlack;
       }
@@ -762,7 +772,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int32_t head_dim, hipStream_t st
   if (a.rows_per_tile == 128) {
     return head_dim == 128 ? launch_typed<128, 4, 64>(a, stream) : launch_typed<64, 4, 64>(a, stream);
   }
-  return head_dim == 128 ? launch_typed<128, 1, 64>(a, stream) : launch_typed<64, 1, 64>(a, stream);
+  return head_dim == 128 ? launch_typed<128, 1, 32>(a, stream) : launch_typed<64, 1, 32>(a, stream);
 }
 
 }  // namespace pa
