@@ -169,6 +169,27 @@ struct TileSrc {
   int start;  // first row of the sequence's new tokens in k/v
   int c;      // cached positions
   int total;  // cached + new positions
+  // Block ids of the cached part, one per lane, 64 at a time: a tile takes
+  // its id with a lane read, so no tile issue waits on a block-table load
+  // (which, in the in-order queue of vector loads, would wait for every tile
+  // load in flight).
+  int win_base;   // first block index held
+  int win_limit;  // blocks of the cached part
+  int win;        // this lane's id: table[win_base + lane]
+
+  // Loads the window at block b and completes it (a rare path: once per
+  // segment and once per 64 blocks).
+  __device__ __forceinline__ void fill(int b, int lane) {
+    win_base = b;
+    win = b + lane < win_limit ? table[b + lane] : 0;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+  __device__ __forceinline__ int block(int b, int lane) {
+    if (b - win_base >= kWave) fill(b, lane);  // wave-uniform, rare
+    return __builtin_amdgcn_readlane(win, b - win_base);
+  }
 };
 
 // Issue the direct-to-LDS loads of key tile kt into one stage ([K tile | V
@@ -178,7 +199,7 @@ struct TileSrc {
 // runs past the last key (its rows re-read the last key), resolves each
 // lane's row on its own.
 template <int D, int NT, int KT>
-__device__ __forceinline__ void issue_tile(const TileSrc<D, NT, KT>& t, int kt, char* stage,
+__device__ __forceinline__ void issue_tile(TileSrc<D, NT, KT>& t, int kt, char* stage,
                                            const int (&krow)[KT * PShape<D, KT>::kPieces / NT],
                                            const int (&kgo)[KT * PShape<D, KT>::kPieces / NT],
                                            const int (&vgo)[KT * PShape<D, KT>::kPieces / NT], int tid,
@@ -195,7 +216,7 @@ __device__ __forceinline__ void issue_tile(const TileSrc<D, NT, KT>& t, int kt, 
     const bf16_t* kb;
     const bf16_t* vb;
     if (in_pool) {
-      const int block = __builtin_amdgcn_readfirstlane(t.table[k0 / kTokensPerBlock]);
+      const int block = t.block(k0 / kTokensPerBlock, tid & (kWave - 1));
       row0 = static_cast<int64_t>(block) * kTokensPerBlock + k0 % kTokensPerBlock;
       kb = t.kpool;
       vb = t.vpool;
@@ -213,7 +234,7 @@ __device__ __forceinline__ void issue_tile(const TileSrc<D, NT, KT>& t, int kt, 
       __builtin_amdgcn_global_load_lds(vb + vgo[it], (lds_void_t*)(vdst + lds_off), 16, 0, kNonTemporal);
     }
   } else {
-    const int block = k0 < t.c ? __builtin_amdgcn_readfirstlane(t.table[k0 / kTokensPerBlock]) : 0;
+    const int block = k0 < t.c ? t.block(k0 / kTokensPerBlock, tid & (kWave - 1)) : 0;
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
       const int kr = krow[it];
@@ -500,6 +521,8 @@ __global__ __launch_bounds__(64 * WM, prefill_workgroups_per_cu<WM>()) void page
     src.start = sg.start;
     src.c = sg.c;
     src.total = total_keys;
+    src.win_limit = (sg.c + kTokensPerBlock - 1) / kTokensPerBlock;
+    src.fill(t_lo * KT / kTokensPerBlock, lane);
     if (t_lo < t_hi) issue_tile<D, NT, KT>(src, t_lo, s_kv[0], krow, kgo, vgo, tid, wave);
     // This wave's query columns: nt in {0,1}, column col.
     int qrow_tok[2];   // token index j of the lane's query column (may be >= n: padding)
