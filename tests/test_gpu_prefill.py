@@ -201,3 +201,15 @@ def test_workspace_reused_across_sizes():
                               c.max_q_len, c.max_context_len, workspace_tensor=ws)
         torch.cuda.synchronize()
         compare(out, oracle_prefill(c), torch.bfloat16)
+
+
+@pytest.mark.parametrize("shape", [(16, 8, 128), (4, 2, 64)], ids=["hq16_hkv8_d128", "hq4_hkv2_d64"])
+@pytest.mark.parametrize("new", [[5, 3, 1], [200, 40, 7]], ids=["verify_rows", "prefill_rows"])
+def test_cached_prefix_beyond_64_blocks(shape, new):
+    """Cached prefixes longer than 64 blocks (16384 tokens): a segment's block
+    ids are read 64 at a time, so these cross a refill of that window."""
+    hq, hkv, d = shape
+    cached = [17000, 16400, 300]
+    say("prefill long prefix", shape, new)
+    c = poisoned(w.build_prefill_case("pf_long", cached, new, hq, hkv, d, torch.bfloat16, 23, with_slots=False))
+    compare(run_prefill(c), oracle_prefill(c), torch.bfloat16)
