@@ -11,4 +11,4 @@ from .paged_attention import (  # noqa: F401
     paged_attn_decode,
     paged_attn_prefill,
 )
-from .rope import rope, rope_angles, rope_kv_store  # noqa: F401
+from .rotary import rope, rope_angles, rope_kv_store  # noqa: F401

@@ -1,4 +1,4 @@
-"""Pins for the fp64 RoPE oracle (oracle/rope.py): facts fixed by the
+"""Pins for the fp64 RoPE oracle (oracle/rotary.py): facts fixed by the
 mathematics of a rotation and by closed-form worked examples of the reading
 the oracle takes (pairs (i, i + D/2), angle p * base^(-2i/D), (a, b) ->
 (a cos t - b sin t, b cos t + a sin t)). The pages only name RoPE ("Nano-vLLM

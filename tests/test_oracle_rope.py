@@ -1,15 +1,15 @@
 """The fp64 RoPE oracle against its pins (tests/pins_rope.py), and mutation
-tests: each plants one plausible mistake in a copy of oracle/rope.py (on the
+tests: each plants one plausible mistake in a copy of oracle/rotary.py (on the
 CPU) and checks that some pin fails."""
 import os
 import types
 
 import pytest
 
-import oracle.rope
+import oracle.rotary
 from pins_rope import PINS
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "rope.py")
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "rotary.py")
 
 MUTATIONS = {
     "interleaved_pairs": ("a, b = x64[..., :half], x64[..., half:]", "a, b = x64[..., 0::2], x64[..., 1::2]"),
@@ -26,14 +26,14 @@ MUTATIONS = {
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
 def test_pin(pin):
-    pin(oracle.rope)
+    pin(oracle.rotary)
 
 
 def _mutant(name):
     old, new = MUTATIONS[name]
     text = open(SRC).read()
     assert old in text, f"mutation anchor for {name} not found"
-    mod = types.ModuleType(f"oracle.rope_mutant_{name}")
+    mod = types.ModuleType(f"oracle.rotary_mutant_{name}")
     mod.__package__ = "oracle"
     exec(compile(text.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
     return mod
