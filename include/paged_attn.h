@@ -102,6 +102,40 @@ pa_status pa_kv_store(void* k_cache, void* v_cache, const void* k, const void* v
                       pa_stream_t stream);
 
 /*
+ * pa_rope_kv_store -- rotary position embedding of the new tokens' q and k,
+ * with the rotated k and the plain v stored into the pools (one pass).
+ *
+ * The pages name RoPE among the features of the model Nano-vLLM serves
+ * ("Nano-vLLM System Architecture Analysis", section "Differences from Normal
+ * nanoGPT Inference", item 6) and store computed K/V via slot_mapping
+ * (section 2, "Attention with Paged Cache"); they give no formula. The
+ * rotation implemented: elements i and i + head_dim/2 of a head row form pair
+ * i (i < head_dim/2); at position p the pair (a, b) becomes
+ * (a cos t - b sin t, b cos t + a sin t) with t = p * rope_theta^(-2i/head_dim).
+ * Every query head and KV head of a token turns the same way; v is not
+ * rotated.
+ *
+ * q            : [num_tokens, num_q_heads, head_dim], read only.
+ * q_out        : [num_tokens, num_q_heads, head_dim], the rotated q; may be q
+ *                itself (in place). Must not overlap k, v or the pools.
+ * k, v         : [num_tokens, num_kv_heads, head_dim], read only.
+ * positions    : int32 [num_tokens], each token's position in its sequence.
+ * slot_mapping : int32 [num_tokens] as in pa_kv_store: the rotated k row and
+ *                the v row of token t go to flat slot slot_mapping[t]; a
+ *                negative entry stores nothing (q is rotated regardless).
+ * rope_theta   : the base of the angles, finite and > 0.
+ * The angles are formed in double precision and reduced modulo 2 pi before
+ * the single-precision rotation, so large positions keep full accuracy.
+ * num_tokens == 0 is a valid no-op. Same dtypes, head dims and error codes as
+ * pa_kv_store; num_q_heads must be a positive multiple of num_kv_heads.
+ */
+pa_status pa_rope_kv_store(void* q_out, void* k_cache, void* v_cache, const void* q, const void* k,
+                           const void* v, const int32_t* positions, const int32_t* slot_mapping,
+                           int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks, float rope_theta,
+                           pa_dtype dtype, pa_stream_t stream);
+
+/*
  * pa_paged_attn_decode -- one query token per sequence attending over its
  * whole paged context.
  *

@@ -1,8 +1,9 @@
 """Paged KV-cache attention for AMD Instinct MI355X (gfx950).
 
 Python binding of libpagedattn.so (C ABI in include/paged_attn.h): the
-slot-mapped KV store, paged decode attention with split-context merging, and
-causal paged prefill / speculative-verify attention. PyTorch supplies device
+slot-mapped KV store (also fused with the rotary embedding of q and k), paged
+decode attention with split-context merging, and causal paged prefill /
+speculative-verify attention. PyTorch supplies device
 memory and the current HIP stream; all computation runs in the HIP kernels.
 """
 from ._lib import (  # noqa: F401
@@ -22,5 +23,6 @@ from ._lib import (  # noqa: F401
     paged_attn_decode,
     paged_attn_prefill,
     prefill_workspace_bytes,
+    rope_kv_store,
     version,
 )

@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "kv_store.hip", "decode.hip", "prefill.hip", "device_info.hip"]
+SOURCES = ["api.hip", "kv_store.hip", "rope_store.hip", "decode.hip", "prefill.hip", "device_info.hip"]
 
 # The packed-fp32 feature is turned off for device code: hipcc -O3 would
 # otherwise form packed fp32 add/mul/fma from ordinary float code.

@@ -106,6 +106,41 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   return decode_workspace(num_seqs, num_q_heads, head_dim, max_context_len);
 }
 
+pa_status pa_rope_kv_store(void* q_out, void* k_cache, void* v_cache, const void* q, const void* k, const void* v,
+                           const int32_t* positions, const int32_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, float rope_theta, pa_dtype dtype, pa_stream_t stream) {
+  if (num_tokens < 0 || num_q_heads <= 0) return PA_ERR_INVALID_ARG;
+  const pa_status st = check_common(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (!isfinite(rope_theta) || !(rope_theta > 0.0f)) return PA_ERR_INVALID_ARG;
+  if (k_cache == nullptr || v_cache == nullptr) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (q_out == nullptr || q == nullptr || k == nullptr || v == nullptr || positions == nullptr ||
+      slot_mapping == nullptr)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(k) ||
+      !aligned16(v))
+    return PA_ERR_INVALID_ARG;
+  pa::RopeStoreArgs a;
+  a.q_out = q_out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.positions = positions;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.base = rope_theta;
+  (void)hipGetLastError();
+  return to_status(pa::launch_rope_kv_store(a, dtype == PA_BF16 ? pa::Dtype::kBF16 : pa::Dtype::kF32, head_dim,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
                                            const int32_t* block_tables, const int32_t* context_lens,
                                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

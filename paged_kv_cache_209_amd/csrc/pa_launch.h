@@ -11,6 +11,23 @@ enum class Dtype { kF32 = 0, kBF16 = 1 };
 hipError_t launch_kv_store(void* k_cache, void* v_cache, const void* k, const void* v, const int32_t* slot_mapping,
                            int32_t num_tokens, int32_t row_bytes, hipStream_t stream);
 
+struct RopeStoreArgs {
+  void* q_out;
+  void* k_cache;
+  void* v_cache;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* positions;
+  const int32_t* slot_mapping;
+  int32_t num_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  float base;  // rope theta
+};
+
+hipError_t launch_rope_kv_store(const RopeStoreArgs& args, Dtype dtype, int32_t head_dim, hipStream_t stream);
+
 struct DecodeArgs {
   void* out;
   const void* q;

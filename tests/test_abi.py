@@ -62,6 +62,30 @@ def test_kv_store_empty_is_noop():
     assert kv(T=0, k=None, v=None, slots=None) == pa.PA_OK
 
 
+def rope(**kw):
+    a = dict(qo=P, kc=P, vc=P, q=P, k=P, v=P, pos=P, slots=P, T=4, hq=8, hkv=2, d=128, bs=256, nb=8, theta=1.0e6,
+             dt=pa.PA_BF16)
+    a.update(kw)
+    return pa.library().pa_rope_kv_store(a["qo"], a["kc"], a["vc"], a["q"], a["k"], a["v"], a["pos"], a["slots"],
+                                         a["T"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["theta"], a["dt"],
+                                         None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(qo=None), INVALID), (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(pos=None), INVALID), (dict(slots=None), INVALID), (dict(kc=None), INVALID), (dict(T=-1), INVALID),
+    (dict(hq=0), INVALID), (dict(hq=6, hkv=4), INVALID), (dict(theta=0.0), INVALID), (dict(theta=-2.0), INVALID),
+    (dict(theta=float("nan")), INVALID), (dict(theta=float("inf")), INVALID), (dict(d=96), UNSUP),
+    (dict(bs=64), UNSUP), (dict(dt=9), INVALID), (dict(qo=P + 4), INVALID), (dict(k=P + 8), INVALID),
+])
+def test_rope_kv_store_validation(kw, expect):
+    assert rope(**kw) == expect
+
+
+def test_rope_kv_store_empty_is_noop():
+    assert rope(T=0, qo=None, q=None, k=None, v=None, pos=None, slots=None) == pa.PA_OK
+
+
 def dec(**kw):
     a = dict(out=P, q=P, kc=P, vc=P, bt=P, cl=P, B=4, hq=8, hkv=2, d=128, bs=256, nb=64, mb=16, mc=4096,
              scale=0.088, dt=pa.PA_BF16, part=0, ws=None, wsb=0)

@@ -1,0 +1,118 @@
+"""Rotary embedding fused with the KV store on the GPU, against the fp64
+oracle (oracle/rotary.py): rotated q, rotated K and plain V rows at the
+stored slots, every other pool row untouched, skipped slots, in-place q, and
+the chunked-prefill workload at full size."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_209_amd as pa
+import workloads as w
+from gpu_util import DEV, bits, compare, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+THETA = 1.0e6
+
+
+def case(seed, t, hq, hkv, d, dtype, nb=6, max_pos=40000):
+    g = torch.Generator().manual_seed(seed)
+    rng = np.random.default_rng(seed)
+    q = torch.randn(t, hq, d, generator=g).to(dtype)
+    k = torch.randn(t, hkv, d, generator=g).to(dtype)
+    v = torch.randn(t, hkv, d, generator=g).to(dtype)
+    kc = torch.randn(nb, 256, hkv, d, generator=g).to(dtype)
+    vc = torch.randn(nb, 256, hkv, d, generator=g).to(dtype)
+    pos = torch.from_numpy(rng.integers(0, max_pos, size=t).astype(np.int32))
+    pos[0] = 0
+    slots = torch.from_numpy(rng.permutation(nb * 256)[:t].astype(np.int32))
+    slots[1::5] = -1
+    return q, k, v, kc, vc, pos, slots
+
+
+def stored_rows(slots):
+    s = [int(x) for x in slots.tolist() if x >= 0]
+    return torch.tensor(s, dtype=torch.long)
+
+
+def check(q, k, v, kc, vc, pos, slots, dtype, in_place=False):
+    ref_q, ref_kc, ref_vc = oracle.rope_kv_store(q, k, v, pos, kc, vc, slots, THETA)
+    ref_q64 = oracle.rope(q, pos, THETA)
+    ref_k64 = oracle.rope(k, pos, THETA)
+    dq, dk, dv, dkc, dvc = to_dev(q), to_dev(k), to_dev(v), to_dev(kc), to_dev(vc)
+    qo = dq if in_place else torch.empty_like(dq)
+    pa.rope_kv_store(qo, dkc, dvc, dq, dk, dv, to_dev(pos), to_dev(slots), THETA)
+    torch.cuda.synchronize()
+    compare(qo, ref_q64, dtype)
+    # pool rows: stored slots hold the rotated k and the plain v, the rest is untouched
+    hkv, d = k.shape[1], k.shape[2]
+    flat_k = dkc.cpu().reshape(-1, hkv, d)
+    flat_v = dvc.cpu().reshape(-1, hkv, d)
+    rows = stored_rows(slots)
+    tok = torch.tensor([i for i, s in enumerate(slots.tolist()) if s >= 0], dtype=torch.long)
+    compare(flat_k[rows], ref_k64[tok], dtype)
+    assert torch.equal(bits(flat_v[rows]), bits(v[tok]))
+    keep = torch.ones(flat_k.shape[0], dtype=torch.bool)
+    keep[rows] = False
+    assert torch.equal(bits(flat_k[keep]), bits(kc.reshape(-1, hkv, d)[keep]))
+    assert torch.equal(bits(flat_v[keep]), bits(vc.reshape(-1, hkv, d)[keep]))
+    # the oracle's own rounding of the stored rows agrees too (same pools elsewhere)
+    assert torch.equal(bits(ref_vc.reshape(-1, hkv, d)[rows]), bits(flat_v[rows]))
+
+
+SHAPES = [(16, 8, 128), (32, 8, 128), (12, 4, 64), (6, 1, 128), (4, 2, 64)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"hq{s[0]}_hkv{s[1]}_d{s[2]}" for s in SHAPES])
+def test_matches_oracle(shape, dtype):
+    hq, hkv, d = shape
+    say("rope store", shape, dtype)
+    check(*case(5, 37, hq, hkv, d, dtype), dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_in_place_query(dtype):
+    say("rope store in place", dtype)
+    check(*case(6, 9, 16, 8, 128, dtype), dtype, in_place=True)
+
+
+def test_position_zero_is_a_plain_store():
+    """At position 0 every angle is 0: q comes back bit for bit and the pools
+    receive exactly what pa_kv_store would store."""
+    say("rope store position zero")
+    q, k, v, kc, vc, pos, slots = case(7, 8, 8, 2, 128, torch.bfloat16)
+    pos.zero_()
+    dq, dkc, dvc = to_dev(q), to_dev(kc), to_dev(vc)
+    qo = torch.empty_like(dq)
+    pa.rope_kv_store(qo, dkc, dvc, dq, to_dev(k), to_dev(v), to_dev(pos), to_dev(slots), THETA)
+    kc2, vc2 = to_dev(kc), to_dev(vc)
+    pa.kv_store(kc2, vc2, to_dev(k), to_dev(v), to_dev(slots))
+    torch.cuda.synchronize()
+    assert torch.equal(bits(qo.cpu()), bits(q))
+    assert torch.equal(bits(dkc.cpu()), bits(kc2.cpu())) and torch.equal(bits(dvc.cpu()), bits(vc2.cpu()))
+
+
+def test_empty():
+    say("rope store empty")
+    q, k, v, kc, vc, pos, slots = case(8, 1, 8, 2, 128, torch.bfloat16)
+    dkc = to_dev(kc)
+    e = torch.empty(0, 8, 128, dtype=torch.bfloat16, device=DEV)
+    ek = torch.empty(0, 2, 128, dtype=torch.bfloat16, device=DEV)
+    ei = torch.empty(0, dtype=torch.int32, device=DEV)
+    pa.rope_kv_store(e, dkc, to_dev(vc), e, ek, ek, ei, ei, THETA)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(dkc.cpu()), bits(kc))
+
+
+def test_chunked_prefill_workload_full_size():
+    """The chunked-prefill workload's 4096 new tokens (8 sequences x 512, 16 Q /
+    8 KV heads, D 128, bf16): positions continue each sequence's cached prefix,
+    1/8 of the slots are -1."""
+    say("rope store c3 full size")
+    c = w.config3()
+    n = (c.cu_seqlens[1:] - c.cu_seqlens[:-1]).tolist()
+    cached = [int(L) - m for L, m in zip(c.context_lens.tolist(), n)]
+    pos = torch.cat([torch.arange(cached[i], cached[i] + n[i], dtype=torch.int32) for i in range(len(n))])
+    check(c.q, c.k, c.v, c.k_cache, c.v_cache, pos, c.slot_mapping, torch.bfloat16)
