@@ -6,10 +6,11 @@ sequences (16 query / 8 KV heads, head_dim 128, bf16, contexts uniform in
 [128, 4096]) over 256-token blocks drawn from a shuffled pool.
 
 The timed region holds exactly --steps steps, bracketed by device
-synchronisation. Pool copies rotate between steps so that a step never finds
-the previous step's K/V in the 256 MB memory-side cache: every step reads its
-K/V from HBM. Per-kernel durations come from HIP events recorded on the stream
-the kernels are launched on.
+synchronisation, with no per-kernel events inside it. Pool copies rotate
+between steps so that a step never finds the previous step's K/V in the 256 MB
+memory-side cache: every step reads its K/V from HBM. Per-kernel durations come
+from separate passes of --steps back-to-back launches of one kernel, bracketed
+by one HIP event pair on the stream the kernels are launched on.
 
 Printed: one JSON line with the headline value (decode-step KV throughput in
 TB/s), the roofline of the decode kernel, the fp64 CPU oracle timed on the
@@ -148,8 +149,30 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.pairs]
 
 
+def time_launches(torch, fn, count):
+    """Average duration (ms) of `count` back-to-back calls of fn(i), bracketed
+    by one HIP event pair on the current stream (the stream the library
+    launches on). Nothing else is enqueued between the calls."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(count):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / count
+
+
 def run_decode_workload(torch, pa, case, steps, warmup, copies, with_store):
-    """Time `steps` decode steps (optionally with the store) on rotating pool copies."""
+    """Time `steps` decode steps (optionally with the store) on rotating pool
+    copies, then the decode launches alone.
+
+    The timed region holds exactly `steps` steps and no per-kernel events (an
+    event pair around each launch adds several microseconds per step on this
+    stack). Kernel durations come from separate passes of `steps` back-to-back
+    launches of one kernel, each bracketed by one event pair on the launch
+    stream."""
     dev = "cuda:0"
     kcs = [case.k_cache.to(dev)]
     vcs = [case.v_cache.to(dev)]
@@ -165,42 +188,42 @@ def run_decode_workload(torch, pa, case, steps, warmup, copies, with_store):
     maxc = case.max_context_len
     ws = pa._lib.workspace(q.device, pa.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim, maxc))
 
-    def step(i, t_dec=None, t_store=None):
-        kc, vc = kcs[i % copies], vcs[i % copies]
+    def store(i):
+        pa.kv_store(kcs[i % copies], vcs[i % copies], kn, vn, sm)
+
+    def decode(i):
+        pa.paged_attn_decode(out, q, kcs[i % copies], vcs[i % copies], bt, cl, case.scale, maxc,
+                             workspace_tensor=ws)
+
+    def step(i):
         if with_store:
-            if t_store:
-                t_store.start()
-            pa.kv_store(kc, vc, kn, vn, sm)
-            if t_store:
-                t_store.stop()
-        if t_dec:
-            t_dec.start()
-        pa.paged_attn_decode(out, q, kc, vc, bt, cl, case.scale, maxc, workspace_tensor=ws)
-        if t_dec:
-            t_dec.stop()
+            store(i)
+        decode(i)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    t_dec, t_store, t_all = Timer(torch), Timer(torch), Timer(torch)
+    t_all = Timer(torch)
     t0 = time.perf_counter()
     t_all.start()
     for i in range(steps):
-        step(warmup + i, t_dec, t_store if with_store else None)
+        step(warmup + i)
     t_all.stop()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    res = {"step_ms": t_all.ms()[0] / steps, "wall_ms": wall * 1e3 / steps, "decode_ms": t_dec.ms()}
+    res = {"step_ms": t_all.ms()[0] / steps, "wall_ms": wall * 1e3 / steps,
+           "decode_ms": time_launches(torch, decode, steps)}
     if with_store:
-        res["store_ms"] = t_store.ms()
+        res["store_ms"] = time_launches(torch, store, steps)
     del kcs, vcs
     torch.cuda.empty_cache()
     return res
 
 
 def run_prefill_workload(torch, pa, case, steps, warmup, with_store):
-    """Time `steps` prefill calls (each preceded by the store of the new tokens
-    when the case has a slot mapping)."""
+    """Average prefill launch time (ms) over `steps` back-to-back launches
+    (the new tokens are stored once beforehand when the case has a slot
+    mapping), and the store's own average when it has one."""
     dev = "cuda:0"
     kc, vc = case.k_cache.to(dev), case.v_cache.to(dev)
     q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
@@ -209,31 +232,56 @@ def run_prefill_workload(torch, pa, case, steps, warmup, with_store):
     sm = case.slot_mapping.to(dev) if with_store else None
     mq, mc = case.max_q_len, case.max_context_len
 
-    def step(t=None):
-        if with_store:
-            pa.kv_store(kc, vc, k, v, sm)
-        if t:
-            t.start()
-        pa.paged_attn_prefill(out, q, k, v, kc, vc, bt, cl, cu, case.scale, mq, mc)
-        if t:
-            t.stop()
+    def store(_i):
+        pa.kv_store(kc, vc, k, v, sm)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t = Timer(torch)
-    for _ in range(steps):
-        step(t)
-    torch.cuda.synchronize()
+    def prefill(_i):
+        pa.paged_attn_prefill(out, q, k, v, kc, vc, bt, cl, cu, case.scale, mq, mc)
+
+    for i in range(warmup):
+        if with_store:
+            store(i)
+        prefill(i)
+    res = {"prefill_ms": time_launches(torch, prefill, steps)}
+    if with_store:
+        res["store_ms"] = time_launches(torch, store, steps)
     del kc, vc
     torch.cuda.empty_cache()
-    return t.ms()
+    return res
 
 
-def median(x):
-    s = sorted(x)
-    n = len(s)
-    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+ROPE_THETA = 1.0e6  # Qwen3's rotary base
+
+
+def run_rope_store(torch, pa, w, steps):
+    """Rotary embedding + KV store of the chunked-prefill workload's 4096 new
+    tokens (16 Q / 8 KV heads, D 128, bf16; positions continue each cached
+    prefix; 1/8 of the slots -1): average launch time and HBM rate of the
+    algorithmic bytes (q read and written, k and v read, stored rows written,
+    positions and slots read)."""
+    c = w.config3()
+    dev = "cuda:0"
+    n = (c.cu_seqlens[1:] - c.cu_seqlens[:-1]).tolist()
+    cached = [int(L) - m for L, m in zip(c.context_lens.tolist(), n)]
+    pos = torch.cat([torch.arange(cached[i], cached[i] + n[i], dtype=torch.int32) for i in range(len(n))])
+    q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+    kc, vc = c.k_cache.to(dev), c.v_cache.to(dev)
+    q_out = torch.empty_like(q)
+    pos_d, sm = pos.to(dev), c.slot_mapping.to(dev)
+
+    def rope(_i):
+        pa.rope_kv_store(q_out, kc, vc, q, k, v, pos_d, sm, ROPE_THETA)
+
+    for i in range(3):
+        rope(i)
+    ms = time_launches(torch, rope, steps)
+    elt = q.element_size()
+    stored = int((c.slot_mapping >= 0).sum())
+    nbytes = (2 * q.numel() + k.numel() + v.numel()) * elt + 2 * stored * k[0].numel() * elt + 2 * 4 * q.shape[0]
+    return {"avg_us": round(ms * 1e3, 2), "TBps": round(nbytes / (ms * 1e-3) / 1e12, 4),
+            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": nbytes, "tokens": int(q.shape[0]), "stored_tokens": stored,
+            "rope_theta": ROPE_THETA}
 
 
 def cpu_baseline(case, budget_s: float):
@@ -272,7 +320,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-secondary", action="store_true")
-    ap.add_argument("--only", default="", help="run just one workload: c2 | c4 | c3 | c5 (profiling)")
+    ap.add_argument("--only", default="", help="run just one workload: c2 | c4 | c3 | rope | c5 (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy --steps times (counter calibration)")
     args = ap.parse_args()
@@ -306,7 +354,7 @@ def main():
         db = decode_bytes(c2)
         store_bytes = 2 * 2 * c2.k_new.numel() * c2.k_new.element_size()  # read + write of k and v rows
         step_bytes = db["total"] + store_bytes
-        dec_ms = sum(r["decode_ms"]) / len(r["decode_ms"])
+        dec_ms = r["decode_ms"]
         value = step_bytes / (r["step_ms"] * 1e-3) / 1e12
         achieved = db["total"] / (dec_ms * 1e-3) / 1e9
         traffic = measured_traffic("decode", "c2")
@@ -344,10 +392,11 @@ def main():
                 "traffic": traffic,
                 "algorithmic_bytes_per_launch": db["total"],
                 "avg_launch_us": round(dec_ms * 1e3, 2),
-                "median_launch_us": round(median(r["decode_ms"]) * 1e3, 2),
+                "timing": f"{args.steps} back-to-back decode launches on the rotating pool copies, one HIP "
+                          "event pair on the launch stream",
             },
             "wall_ms_per_step": round(r["wall_ms"], 5),
-            "store_avg_us": round(sum(r["store_ms"]) / len(r["store_ms"]) * 1e3, 2),
+            "store_avg_us": round(r["store_ms"] * 1e3, 2),
         }
     else:
         result = {"metric": METRIC, "value": None, "note": f"--only {args.only}"}
@@ -356,7 +405,7 @@ def main():
         c4 = w.config4(device="cuda:0")
         r4 = run_decode_workload(torch, pa, c4, max(5, args.steps // 5), 2, 1, with_store=False)
         db4 = decode_bytes(c4)
-        ms = sum(r4["decode_ms"]) / len(r4["decode_ms"])
+        ms = r4["decode_ms"]
         secondary["c4_qwen3_8b_decode_shared_prefix"] = {
             "decode_avg_us": round(ms * 1e3, 1),
             "unique_kv_TBps": round(db4["total"] / (ms * 1e-3) / 1e12, 4),
@@ -370,23 +419,25 @@ def main():
 
     if not args.skip_secondary and args.only in ("", "c3"):
         c3 = w.config3(device="cuda:0")
-        ms = run_prefill_workload(torch, pa, c3, max(10, args.steps), 3, with_store=True)
-        avg = sum(ms) / len(ms)
+        r3 = run_prefill_workload(torch, pa, c3, max(10, args.steps), 3, with_store=True)
+        avg = r3["prefill_ms"]
         fl = prefill_flops(c3)
         pb = prefill_bytes(c3)
         secondary["c3_chunked_prefill_prefix_cache"] = {
             "prefill_avg_us": round(avg * 1e3, 2),
-            "prefill_median_us": round(median(ms) * 1e3, 2),
+            "store_avg_us": round(r3["store_ms"] * 1e3, 2),
             "TFLOPs": round(fl / (avg * 1e-3) / 1e12, 2),
             "frac_mfma_bf16_peak": round(fl / (avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "flops": fl,
             "algorithmic_bytes": pb["total"],
         }
         del c3
+    if not args.skip_secondary and args.only in ("", "c3", "rope"):
+        secondary["c3_rope_kv_store"] = run_rope_store(torch, pa, w, max(10, args.steps))
+        torch.cuda.empty_cache()
     if not args.skip_secondary and args.only in ("", "c5"):
         c5 = w.config5(device="cuda:0")
-        ms = run_prefill_workload(torch, pa, c5, max(5, args.steps // 5), 2, with_store=False)
-        avg = sum(ms) / len(ms)
+        avg = run_prefill_workload(torch, pa, c5, max(5, args.steps // 5), 2, with_store=False)["prefill_ms"]
         fl = prefill_flops(c5)
         pb = prefill_bytes(c5)
         secondary["c5_spec_verify"] = {
