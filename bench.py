@@ -284,6 +284,70 @@ def run_rope_store(torch, pa, w, steps):
             "rope_theta": ROPE_THETA}
 
 
+def run_block_manager(w, num_seqs, lo, hi, seed, steps, with_oracle):
+    """Host time of one decode step's metadata from the native block manager
+    (append one token to every sequence, then prepare_decode), on num_seqs
+    sequences with contexts uniform in [lo, hi] and 256-token blocks, the
+    odd-numbered ones longer than 1024 tokens opening with one shared
+    1024-token system prompt; the plain-Python oracle of the
+    same manager is timed on the same steps when with_oracle is set."""
+    import numpy as np
+
+    import oracle.block_manager as obm
+    from paged_kv_cache_209_amd.block_manager import BlockManager
+
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(lo, hi, endpoint=True, size=num_seqs)
+    system = [int(x) for x in rng.integers(0, 150000, size=1024)]
+    prompts = []
+    for i, L in enumerate(lens):
+        share = i % 2 == 1 and L > 1024
+        tail = [int(x) for x in rng.integers(0, 150000, size=int(L) - (1024 if share else 0))]
+        prompts.append((system if share else []) + tail)
+    nb = int(1.25 * sum(-(-len(p) // 256) for p in prompts)) + num_seqs * ((steps + 3) // 256 + 2)
+    width = max(-(-len(p) // 256) for p in prompts) + (steps + 3) // 256 + 2
+    res = {}
+    impls = [("native", BlockManager(nb, 256))]
+    if with_oracle:
+        impls.append(("oracle", obm.OracleBlockManager(nb, 256)))
+    for name, m in impls:
+        for i, p in enumerate(prompts):
+            m.allocate(i, p)
+        ids = list(range(num_seqs))
+        if name == "native":
+            m.prepare_prefill(ids, width)
+        else:
+            m.prepare_prefill(ids, None, width, 1 << 30)
+        if name == "native":
+            import torch
+
+            id_t = torch.arange(num_seqs, dtype=torch.int64)
+            tok_t = torch.full((num_seqs,), 7, dtype=torch.int32)
+            bufs = {"positions": torch.empty(num_seqs, dtype=torch.int32),
+                    "slot_mapping": torch.empty(num_seqs, dtype=torch.int32),
+                    "context_lens": torch.empty(num_seqs, dtype=torch.int32),
+                    "block_tables": torch.empty((num_seqs, width), dtype=torch.int32)}
+            for _ in range(3):
+                m.append_tokens(id_t, tok_t)
+                m.prepare_decode(id_t, width, out=bufs)
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                m.append_tokens(id_t, tok_t)
+                m.prepare_decode(id_t, width, out=bufs)
+        else:
+            toks = [7] * num_seqs
+            for _ in range(3):
+                m.append_tokens(ids, toks)
+                m.prepare_decode(ids, width)
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                m.append_tokens(ids, toks)
+                m.prepare_decode(ids, width)
+        res[f"{name}_us_per_step"] = round((time.perf_counter() - t0) / steps * 1e6, 1)
+    res.update({"num_seqs": num_seqs, "context_range": [lo, hi], "steps": steps, "num_blocks": nb})
+    return res
+
+
 def cpu_baseline(case, budget_s: float):
     """The fp64 oracle (unchanged) on the host cores, on whole decode steps of
     the same workload (store + decode), repeated until `budget_s` has passed."""
@@ -320,7 +384,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-secondary", action="store_true")
-    ap.add_argument("--only", default="", help="run just one workload: c2 | c4 | c3 | rope | c5 (profiling)")
+    ap.add_argument("--only", default="", help="run just one workload: c2 | c4 | c3 | rope | c5 | bm (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy --steps times (counter calibration)")
     args = ap.parse_args()
@@ -451,6 +515,11 @@ def main():
         }
         del c5
         torch.cuda.empty_cache()
+    if not args.skip_secondary and args.only in ("", "bm"):
+        secondary["block_manager_decode_step_host"] = {
+            "c2_shape": run_block_manager(w, 64, 128, 4096, 1, 200, with_oracle=True),
+            "c4_shape": run_block_manager(w, 256, 1024, 8192, 3, 200, with_oracle=False),
+        }
     if secondary:
         result["secondary"] = secondary
     if not args.skip_cpu and args.only in ("", "c2"):

@@ -67,7 +67,8 @@ typedef enum {
   PA_ERR_INVALID_ARG = -1, /* null pointer, non-positive or inconsistent size */
   PA_ERR_UNSUPPORTED = -2, /* valid but not built: dtype, head_dim, block_size */
   PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
-  PA_ERR_HIP = -4          /* the HIP runtime reported a launch error */
+  PA_ERR_HIP = -4,         /* the HIP runtime reported a launch error */
+  PA_ERR_NO_BLOCKS = -5    /* block manager: too few free blocks (preempt, retry) */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;

@@ -3,7 +3,8 @@
 Python binding of libpagedattn.so (C ABI in include/paged_attn.h): the
 slot-mapped KV store (also fused with the rotary embedding of q and k), paged
 decode attention with split-context merging, and causal paged prefill /
-speculative-verify attention. PyTorch supplies device
+speculative-verify attention, and the host block manager that emits
+the block tables and slot mappings (`block_manager.BlockManager`). PyTorch supplies device
 memory and the current HIP stream; all computation runs in the HIP kernels.
 """
 from ._lib import (  # noqa: F401
@@ -11,6 +12,7 @@ from ._lib import (  # noqa: F401
     PA_BF16,
     PA_ERR_HIP,
     PA_ERR_INVALID_ARG,
+    PA_ERR_NO_BLOCKS,
     PA_ERR_UNSUPPORTED,
     PA_ERR_WORKSPACE,
     PA_F32,

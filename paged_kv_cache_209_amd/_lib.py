@@ -21,6 +21,7 @@ PA_ERR_INVALID_ARG = -1
 PA_ERR_UNSUPPORTED = -2
 PA_ERR_WORKSPACE = -3
 PA_ERR_HIP = -4
+PA_ERR_NO_BLOCKS = -5
 
 PA_F32 = 0
 PA_BF16 = 1
@@ -28,6 +29,7 @@ PA_BF16 = 1
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
 
 _i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
 _sz = ctypes.c_size_t
 _f32 = ctypes.c_float
@@ -48,6 +50,21 @@ SIGNATURES = {
     "pa_paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    # host-side block manager (include/block_manager.h)
+    "pa_xxh64": (ctypes.c_uint64, [_vp, _sz, ctypes.c_uint64]),
+    "pa_bm_create": (_i32, [_i32, _i32, _vp]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_num_free_blocks": (_i32, [_vp]),
+    "pa_bm_ref_count": (_i32, [_vp, _i32]),
+    "pa_bm_allocate": (_i32, [_vp, _i64, _vp, _i32, _vp]),
+    "pa_bm_can_allocate": (_i32, [_vp, _vp, _i32, _vp]),
+    "pa_bm_append_token": (_i32, [_vp, _i64, _i32]),
+    "pa_bm_append_tokens": (_i32, [_vp, _vp, _vp, _i32]),
+    "pa_bm_free": (_i32, [_vp, _i64]),
+    "pa_bm_seq_info": (_i32, [_vp, _i64, _vp, _vp, _vp]),
+    "pa_bm_block_table": (_i32, [_vp, _i64, _vp, _i32]),
+    "pa_bm_prepare_prefill": (_i32, [_vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "pa_bm_prepare_decode": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None

@@ -20,6 +20,9 @@ LIB = os.path.join(PKG, "libpagedattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "kv_store.hip", "rope_store.hip", "decode.hip", "prefill.hip", "device_info.hip"]
+# host-only C++ (no device code): built with the host compiler
+HOST_SOURCES = ["block_manager.cpp"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE]
 
 # The packed-fp32 feature is turned off for device code: hipcc -O3 would
 # otherwise form packed fp32 add/mul/fma from ordinary float code.
@@ -62,6 +65,13 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        raise RuntimeError("no host C++ compiler (g++) found")
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
+        objs.append(obj)
+        cmds.append([cxx, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         outs = list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"

@@ -69,6 +69,8 @@ const char* pa_status_string(pa_status status) {
       return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP:
       return "PA_ERR_HIP: HIP runtime error";
+    case PA_ERR_NO_BLOCKS:
+      return "PA_ERR_NO_BLOCKS: too few free KV-cache blocks";
   }
   return "unknown pa_status";
 }
