@@ -284,6 +284,80 @@ def run_rope_store(torch, pa, w, steps):
             "rope_theta": ROPE_THETA}
 
 
+def run_decode_graphs(torch, pa, steps):
+    """Decode steps (store of the new tokens + paged decode) issued eagerly
+    (two binding calls per step, exact max context) and as one graph launch
+    per step (bucket graphs captured for the table's 4096-token bound), at
+    batch sizes 1, 4, 16 and 64 of Qwen3-0.6B-shaped sequences (16 Q / 8 KV
+    heads, D 128, bf16, contexts uniform in [128, 4096]). Per step: wall time
+    of `steps` back-to-back steps (host issue included) and GPU time from one
+    event pair around them."""
+    import numpy as np
+
+    from paged_kv_cache_209_amd.decode_graphs import DecodeGraphs
+
+    dev = "cuda:0"
+    hq, hkv, d, bs, mb, maxb = 16, 8, 128, 256, 16, 64
+    rng = np.random.default_rng(7)
+    ctx = rng.integers(128, 4096, endpoint=True, size=maxb).astype(np.int32)
+    need = [-(-int(c) // bs) for c in ctx]
+    nb = int(1.25 * sum(need)) + 1
+    ids = rng.permutation(nb)[:sum(need)]
+    bt = np.full((maxb, mb), -1, dtype=np.int32)
+    slots = np.empty(maxb, dtype=np.int32)
+    k = 0
+    for i, c in enumerate(ctx):
+        bt[i, :need[i]] = ids[k:k + need[i]]
+        k += need[i]
+        slots[i] = bt[i, (c - 1) // bs] * bs + (c - 1) % bs
+    g = torch.Generator(device=dev).manual_seed(7)
+    kc = torch.randn((nb, bs, hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    vc = torch.randn((nb, bs, hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    ws_bytes = pa.decode_workspace_bytes(maxb, hq, d, mb * bs)
+    bufs = {"out": torch.zeros((maxb, hq, d), dtype=torch.bfloat16, device=dev),
+            "q": torch.randn((maxb, hq, d), generator=g, device=dev).to(torch.bfloat16),
+            "k_new": torch.randn((maxb, hkv, d), generator=g, device=dev).to(torch.bfloat16),
+            "v_new": torch.randn((maxb, hkv, d), generator=g, device=dev).to(torch.bfloat16),
+            "slot_mapping": torch.from_numpy(slots).to(dev),
+            "block_tables": torch.from_numpy(bt).to(dev),
+            "context_lens": torch.from_numpy(ctx).to(dev),
+            "k_cache": kc, "v_cache": vc,
+            "workspace": torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)}
+    graphs = DecodeGraphs(bufs, d ** -0.5)
+    eager_ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    res = {}
+    for n in (1, 4, 16, 64):
+        sm, ctx_n = bufs["slot_mapping"][:n].clone(), bufs["context_lens"][:n].clone()
+        maxc = int(ctx[:n].max())
+
+        def eager(_i):
+            pa.kv_store(kc, vc, bufs["k_new"][:n], bufs["v_new"][:n], sm)
+            pa.paged_attn_decode(bufs["out"][:n], bufs["q"][:n], kc, vc, bufs["block_tables"][:n], ctx_n,
+                                 d ** -0.5, maxc, workspace_tensor=eager_ws)
+
+        def graph(_i):
+            graphs.launch(n)
+
+        row = {}
+        for name, fn in (("eager", eager), ("graph", graph)):
+            for i in range(5):
+                fn(i)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            ms = time_launches(torch, fn, steps)
+            row[f"{name}_wall_us"] = round((time.perf_counter() - t0) / steps * 1e6, 2)
+            row[f"{name}_gpu_us"] = round(ms * 1e3, 2)
+            # padding rows of the graph's buckets are reset by each launch; restore them
+            bufs["slot_mapping"].copy_(torch.from_numpy(slots).to(dev))
+            bufs["context_lens"].copy_(torch.from_numpy(ctx).to(dev))
+        row["bucket"] = graphs.bucket(n)
+        res[f"batch_{n}"] = row
+    graphs.close()
+    del kc, vc, bufs
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_block_manager(w, num_seqs, lo, hi, seed, steps, with_oracle):
     """Host time of one decode step's metadata from the native block manager
     (append one token to every sequence, then prepare_decode), on num_seqs
@@ -384,7 +458,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-secondary", action="store_true")
-    ap.add_argument("--only", default="", help="run just one workload: c2 | c4 | c3 | rope | c5 | bm (profiling)")
+    ap.add_argument("--only", default="", help="run just one workload: c2 | c4 | c3 | rope | c5 | graphs | bm (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy --steps times (counter calibration)")
     args = ap.parse_args()
@@ -515,6 +589,8 @@ def main():
         }
         del c5
         torch.cuda.empty_cache()
+    if not args.skip_secondary and args.only in ("", "graphs"):
+        secondary["decode_step_graphs_vs_eager"] = run_decode_graphs(torch, pa, max(50, args.steps))
     if not args.skip_secondary and args.only in ("", "bm"):
         secondary["block_manager_decode_step_host"] = {
             "c2_shape": run_block_manager(w, 64, 128, 4096, 1, 200, with_oracle=True),

@@ -252,6 +252,65 @@ pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const v
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_q_len, int32_t max_context_len);
 
+/*
+ * Decode-step graphs -- the store of the step's new K/V followed by paged
+ * decode, captured once as HIP graphs for batch buckets 1, 2, 4, ... up to
+ * max_batch (<= 512; the last bucket is max_batch itself) and replayed with
+ * one launch per step.
+ *
+ * Defined by "Nano-vLLM System Architecture Analysis", section 2 "CUDA
+ * Graphs" (decode steps captured as graphs, eager mode beyond 512 sequences)
+ * and "Differences from Normal nanoGPT Inference", item 4 (graphs captured
+ * for batch sizes 1, 2, 4, 8, ... 512; a step runs the closest one that
+ * holds it).
+ *
+ * The graphs read and write the static buffers named at creation (device
+ * pointers, rows for max_batch sequences, layouts as for pa_kv_store and
+ * pa_paged_attn_decode). Before each launch the caller writes the first
+ * num_seqs rows of q, k_new, v_new, slot_mapping, block_tables and
+ * context_lens. The launch then makes rows num_seqs .. bucket-1 inert
+ * (slot -1: nothing stored; context 0: no output written) with a small
+ * kernel on `stream`, and replays the bucket's graph on `stream`: out rows
+ * 0 .. num_seqs-1 receive the step's attention. Contexts may be up to
+ * max_blocks_per_seq * block_size tokens (the graphs are captured for that
+ * bound). The workspace follows the decode rule (zero-filled before the first
+ * launch, sized by pa_decode_workspace_bytes(max_batch, num_q_heads,
+ * head_dim, 0, max_blocks_per_seq * block_size)); launches on one graph set
+ * must not overlap. num_seqs > max_batch returns PA_ERR_INVALID_ARG (run
+ * eagerly instead); num_seqs == 0 is a no-op.
+ */
+typedef struct pa_decode_graphs pa_decode_graphs;
+
+typedef struct {
+  void* out;                   /* [max_batch, num_q_heads, head_dim] */
+  const void* q;               /* [max_batch, num_q_heads, head_dim] */
+  const void* k_new;           /* [max_batch, num_kv_heads, head_dim] */
+  const void* v_new;           /* [max_batch, num_kv_heads, head_dim] */
+  int32_t* slot_mapping;       /* [max_batch] */
+  const int32_t* block_tables; /* [max_batch, max_blocks_per_seq] */
+  int32_t* context_lens;       /* [max_batch] */
+  void* k_cache;               /* [num_blocks, block_size, num_kv_heads, head_dim] */
+  void* v_cache;
+  void* workspace;
+  size_t workspace_bytes;
+} pa_decode_graph_buffers;
+
+/* Captures the bucket graphs (nothing runs). *out receives the handle. The
+ * capture uses a stream of the library's own; `bufs` is copied. */
+pa_status pa_decode_graphs_create(const pa_decode_graph_buffers* bufs, int32_t max_batch, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, float scale, pa_dtype dtype,
+                                  pa_decode_graphs** out);
+
+/* One decode step over the first num_seqs rows (see above). */
+pa_status pa_decode_graphs_launch(pa_decode_graphs* graphs, int32_t num_seqs, pa_stream_t stream);
+
+/* The bucket a step of num_seqs sequences runs in; 0 when none holds it. */
+int32_t pa_decode_graphs_bucket(const pa_decode_graphs* graphs, int32_t num_seqs);
+
+/* Releases the graphs. NULL is a no-op. */
+void pa_decode_graphs_destroy(pa_decode_graphs* graphs);
+
 #ifdef __cplusplus
 }
 #endif

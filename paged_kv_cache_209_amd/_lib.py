@@ -50,6 +50,11 @@ SIGNATURES = {
     "pa_paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    # decode-step graphs (the buffer struct and the handle are passed by address)
+    "pa_decode_graphs_create": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
+    "pa_decode_graphs_launch": (_i32, [_vp, _i32, _vp]),
+    "pa_decode_graphs_bucket": (_i32, [_vp, _i32]),
+    "pa_decode_graphs_destroy": (None, [_vp]),
     # host-side block manager (include/block_manager.h)
     "pa_xxh64": (ctypes.c_uint64, [_vp, _sz, ctypes.c_uint64]),
     "pa_bm_create": (_i32, [_i32, _i32, _vp]),

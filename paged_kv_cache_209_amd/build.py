@@ -19,7 +19,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "kv_store.hip", "rope_store.hip", "decode.hip", "prefill.hip", "device_info.hip"]
+SOURCES = ["api.hip", "kv_store.hip", "rope_store.hip", "decode.hip", "prefill.hip", "device_info.hip",
+           "decode_graphs.hip"]
 # host-only C++ (no device code): built with the host compiler
 HOST_SOURCES = ["block_manager.cpp"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE]
