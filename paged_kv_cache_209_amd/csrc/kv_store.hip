@@ -2,12 +2,12 @@
 // caller's slot mapping names ("Nano-vLLM System Architecture Analysis",
 // section 2, "Attention with Paged Cache": computed K/V entries are stored into
 // the paged cache via slot_mapping). Pure data movement. The new tokens' K (and
-// V) rows form one flat array of 16-byte pieces; a workgroup moves
-// kStorePieces sweeps of 256 consecutive pieces (each sweep fully coalesced),
-// issuing every load of all its sweeps -- the slots and the K and V pieces --
-// before the first store, so a thread keeps 2 * kStorePieces 16-byte loads in
-// flight instead of one load waiting behind its slot. Pieces of a token whose
-// slot is negative are read but not stored.
+// V) rows form one flat array of 16-byte pieces; a workgroup moves 1 or 4
+// sweeps of 256 consecutive pieces (each sweep fully coalesced), issuing every
+// load of its sweeps -- the slots and the K and V pieces -- before the first
+// store, so no K/V load waits behind its slot and a thread of a large store
+// keeps 8 16-byte loads in flight. Pieces of a token whose slot is negative
+// are read but not stored.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -16,8 +16,11 @@ namespace pa {
 namespace {
 
 constexpr int kStoreThreads = 256;
-constexpr int kStorePieces = 4;  // sweeps per workgroup
 
+// kStorePieces sweeps per workgroup: 4 for large stores, 1 for small ones,
+// where spreading the few pieces over more compute units matters more than
+// loads in flight per thread.
+template <int kStorePieces>
 __global__ __launch_bounds__(kStoreThreads) void kv_store_kernel(u32x4_t* __restrict__ k_cache,
                                                                 u32x4_t* __restrict__ v_cache,
                                                                 const u32x4_t* __restrict__ k,
@@ -57,11 +60,21 @@ hipError_t launch_kv_store(void* k_cache, void* v_cache, const void* k, const vo
   const int32_t pieces_per_row = row_bytes / 16;
   const int64_t total = static_cast<int64_t>(num_tokens) * pieces_per_row;
   if (total == 0) return hipSuccess;
-  const int64_t per_block = static_cast<int64_t>(kStoreThreads) * kStorePieces;
-  const int64_t blocks = (total + per_block - 1) / per_block;
-  kv_store_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(kStoreThreads), 0, stream>>>(
-      static_cast<u32x4_t*>(k_cache), static_cast<u32x4_t*>(v_cache), static_cast<const u32x4_t*>(k),
-      static_cast<const u32x4_t*>(v), slot_mapping, total, pieces_per_row);
+  // Four sweeps per workgroup once that still gives at least 256 workgroups.
+  constexpr int64_t kLarge = int64_t{256} * kStoreThreads * 4;
+  u32x4_t* kc = static_cast<u32x4_t*>(k_cache);
+  u32x4_t* vc = static_cast<u32x4_t*>(v_cache);
+  const u32x4_t* kk = static_cast<const u32x4_t*>(k);
+  const u32x4_t* vv = static_cast<const u32x4_t*>(v);
+  if (total >= kLarge) {
+    const int64_t blocks = (total + kStoreThreads * 4 - 1) / (kStoreThreads * 4);
+    kv_store_kernel<4><<<dim3(static_cast<uint32_t>(blocks)), dim3(kStoreThreads), 0, stream>>>(
+        kc, vc, kk, vv, slot_mapping, total, pieces_per_row);
+  } else {
+    const int64_t blocks = (total + kStoreThreads - 1) / kStoreThreads;
+    kv_store_kernel<1><<<dim3(static_cast<uint32_t>(blocks)), dim3(kStoreThreads), 0, stream>>>(
+        kc, vc, kk, vv, slot_mapping, total, pieces_per_row);
+  }
   return hipGetLastError();
 }
 
