@@ -42,7 +42,7 @@ TOKENS_PER_BLOCK = 256
 def _bits(t: torch.Tensor) -> torch.Tensor:
     """Same-size integer view, so that copies move raw bits (NaN payloads kept)."""
     size = t.element_size()
-    return t.view({2: torch.int16, 4: torch.int32, 8: torch.int64}[size])
+    return t.view({1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[size])
 
 
 def kv_store(k_cache: torch.Tensor, v_cache: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
