@@ -253,6 +253,45 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
                                   int32_t max_q_len, int32_t max_context_len);
 
 /*
+ * fp8 KV cache. The pages mention quantised KV-cache transfers ("Why
+ * Understand Inference Engine Architecture?", Tensor Parallelism
+ * Optimization, item 3) but fix no format. Reading taken: codes are OCP FP8
+ * E4M3 (bias 7, subnormals, S.1111.111 = NaN, largest finite 448), one code
+ * per element, pools uint8 [num_blocks, 256, num_kv_heads, head_dim] with one
+ * fp32 scale per pool (k_scale, v_scale > 0, finite). Element x is stored as
+ * the code nearest to clamp(fp32(x) * fp32(1/s), -448, 448), ties to even
+ * (1/s formed in fp32 by the library); code c reads back as value(c) * s.
+ * Supported: head_dim 128, bf16 k/v/q/out.
+ */
+
+/* pa_kv_store with quantisation: bf16 k, v [num_tokens, num_kv_heads, 128]
+ * become fp8 codes at the slots slot_mapping names (negative: not stored).
+ * The codes are a deterministic function of the inputs (bit-exact). */
+pa_status pa_kv_store_fp8(void* k_cache, void* v_cache, const void* k, const void* v,
+                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks, float k_scale,
+                          float v_scale, pa_stream_t stream);
+
+/* Workspace bytes of pa_paged_attn_decode_fp8: one partial (max, sum and
+ * head_dim fp32 values) per (sequence, 256-token block, query head). Needs no
+ * clearing. 0 for unsupported sizes. */
+size_t pa_decode_fp8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                     int32_t max_context_len);
+
+/* pa_paged_attn_decode over fp8 pools: q and out bf16 [num_seqs,
+ * num_q_heads, 128]; attention over the dequantised K/V (score =
+ * scale * q.(code_k * k_scale), output = sum p (code_v * v_scale) / sum p),
+ * fp32 accumulation, bf16 output rounded to nearest-even. Two launches on
+ * `stream`: per-block partials, then an in-order merge (results bit-identical
+ * from run to run). Same argument rules as pa_paged_attn_decode. */
+pa_status pa_paged_attn_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                   int32_t max_context_len, float scale, float k_scale, float v_scale,
+                                   void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
  * Decode-step graphs -- the store of the step's new K/V followed by paged
  * decode, captured once as HIP graphs for batch buckets 1, 2, 4, ... up to
  * max_batch (<= 512; the last bucket is max_batch itself) and replayed with

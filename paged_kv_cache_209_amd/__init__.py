@@ -18,11 +18,14 @@ from ._lib import (  # noqa: F401
     PA_F32,
     PA_OK,
     PagedAttnError,
+    decode_fp8_workspace_bytes,
     decode_num_workgroups,
     decode_workspace_bytes,
     kv_store,
+    kv_store_fp8,
     library,
     paged_attn_decode,
+    paged_attn_decode_fp8,
     paged_attn_prefill,
     prefill_workspace_bytes,
     rope_kv_store,

@@ -50,6 +50,10 @@ SIGNATURES = {
     "pa_paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_kv_store_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _vp]),
+    "pa_decode_fp8_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "pa_paged_attn_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _f32, _f32, _f32, _vp, _sz, _vp]),
     # decode-step graphs (the buffer struct and the handle are passed by address)
     "pa_decode_graphs_create": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
     "pa_decode_graphs_launch": (_i32, [_vp, _i32, _vp]),
@@ -186,6 +190,57 @@ def rope_kv_store(q_out: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _check(library().pa_rope_kv_store(_ptr(q_out), _ptr(k_cache), _ptr(v_cache), _ptr(q), _ptr(k), _ptr(v),
                                       _ptr(positions), _ptr(slot_mapping), q.shape[0], q.shape[1], hkv, d, bs, nb,
                                       float(rope_theta), _dtype_code(k_cache), _stream(k_cache)), "pa_rope_kv_store")
+
+
+def kv_store_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 slot_mapping: torch.Tensor, k_scale: float, v_scale: float) -> None:
+    """pa_kv_store_fp8: bf16 k/v rows quantised to E4M3 codes (uint8 pools,
+    one fp32 scale per pool) at slot_mapping."""
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, name, torch.uint8)
+    for name, t in (("k", k), ("v", v)):
+        _dev_tensor(t, name, torch.bfloat16)
+    _dev_tensor(slot_mapping, "slot_mapping", torch.int32)
+    nb, bs, hkv, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or k.shape != v.shape or k.dim() != 3 or k.shape[1:] != (hkv, d):
+        raise ValueError("kv_store_fp8: pools [NB, 256, Hkv, D] and k/v [T, Hkv, D] expected")
+    if slot_mapping.shape != (k.shape[0],):
+        raise ValueError("kv_store_fp8: slot_mapping must be [T]")
+    _check(library().pa_kv_store_fp8(_ptr(k_cache), _ptr(v_cache), _ptr(k), _ptr(v), _ptr(slot_mapping), k.shape[0],
+                                     hkv, d, bs, nb, float(k_scale), float(v_scale), _stream(k_cache)),
+           "pa_kv_store_fp8")
+
+
+def decode_fp8_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int) -> int:
+    return int(library().pa_decode_fp8_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len))
+
+
+def paged_attn_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, k_scale: float,
+                          v_scale: float, max_context_len: int,
+                          workspace_tensor: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """pa_paged_attn_decode_fp8: bf16 out[B, Hq, D] = attention of bf16 q over
+    the dequantised fp8 pools."""
+    for name, t in (("out", out), ("q", q)):
+        _dev_tensor(t, name, torch.bfloat16)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, name, torch.uint8)
+    _dev_tensor(block_tables, "block_tables", torch.int32)
+    _dev_tensor(context_lens, "context_lens", torch.int32)
+    nb, bs, hkv, d = k_cache.shape
+    b, hq, dq = q.shape
+    if out.shape != q.shape or dq != d or v_cache.shape != k_cache.shape or block_tables.dim() != 2 \
+            or block_tables.shape[0] != b or context_lens.shape != (b,):
+        raise ValueError("paged_attn_decode_fp8: shapes do not match")
+    need = decode_fp8_workspace_bytes(b, hq, d, max_context_len)
+    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need, kind="decode_fp8")
+    ws_ptr = None if ws is None else ws.data_ptr()
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(library().pa_paged_attn_decode_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                              _ptr(context_lens), b, hq, hkv, d, bs, nb, block_tables.shape[1],
+                                              int(max_context_len), float(scale), float(k_scale), float(v_scale),
+                                              ws_ptr, ws_bytes, _stream(q)), "pa_paged_attn_decode_fp8")
+    return out
 
 
 def decode_num_workgroups(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_context_len: int,

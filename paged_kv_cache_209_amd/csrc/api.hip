@@ -208,6 +208,75 @@ pa_status pa_paged_attn_decode(void* out, const void* q, const void* k_cache, co
                                           workspace_bytes, stream);
 }
 
+pa_status pa_kv_store_fp8(void* k_cache, void* v_cache, const void* k, const void* v, const int32_t* slot_mapping,
+                          int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t num_blocks, float k_scale, float v_scale, pa_stream_t stream) {
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  const pa_status st = check_common(num_kv_heads, head_dim, block_size, num_blocks, PA_BF16);
+  if (st != PA_OK) return st;
+  if (head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!isfinite(k_scale) || !isfinite(v_scale) || !(k_scale > 0.0f) || !(v_scale > 0.0f)) return PA_ERR_INVALID_ARG;
+  if (k_cache == nullptr || v_cache == nullptr) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (k == nullptr || v == nullptr || slot_mapping == nullptr) return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k) || !aligned16(v)) return PA_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return to_status(pa::launch_kv_store_fp8(k_cache, v_cache, k, v, slot_mapping, num_tokens, num_kv_heads * head_dim,
+                                           1.0f / k_scale, 1.0f / v_scale, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_fp8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                     int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim != 128 || max_context_len <= 0) return 0;
+  return pa::decode_fp8_workspace_layout(num_seqs, num_q_heads, ceil_div(max_context_len, kBlockSize)).total;
+}
+
+pa_status pa_paged_attn_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                   int32_t max_context_len, float scale, float k_scale, float v_scale,
+                                   void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  if (num_seqs < 0 || num_q_heads <= 0) return PA_ERR_INVALID_ARG;
+  const pa_status st = check_common(num_kv_heads, head_dim, block_size, num_blocks, PA_BF16);
+  if (st != PA_OK) return st;
+  if (head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (max_blocks_per_seq <= 0 || max_context_len <= 0) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !isfinite(k_scale) || !isfinite(v_scale) || !(k_scale > 0.0f) || !(v_scale > 0.0f))
+    return PA_ERR_INVALID_ARG;
+  if (k_cache == nullptr || v_cache == nullptr) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (out == nullptr || q == nullptr || block_tables == nullptr || context_lens == nullptr) return PA_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID_ARG;
+  const int32_t max_blocks = static_cast<int32_t>(ceil_div(max_context_len, kBlockSize));
+  const pa::WorkspaceLayout lay = pa::decode_fp8_workspace_layout(num_seqs, num_q_heads, max_blocks);
+  if (workspace == nullptr || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
+  pa::DecodeFp8Args a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.max_blocks = max_blocks;
+  a.scale_log2 = scale * k_scale * kLog2e;
+  a.v_scale = v_scale;
+  char* ws = static_cast<char*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(ws + lay.lse_off);
+  a.part_acc = reinterpret_cast<float*>(ws + lay.out_off);
+  (void)hipGetLastError();
+  return to_status(pa::launch_decode_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_q_len,
                                   int32_t max_context_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_q_len <= 0 || max_context_len <= 0) return 0;

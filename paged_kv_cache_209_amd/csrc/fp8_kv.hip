@@ -1,0 +1,295 @@
+// fp8 KV cache: a quantising store and decode attention that reads the fp8
+// pools (half the bytes of bf16) and dequantises on the fly. The pages name
+// quantised KV-cache transfers ("Why Understand Inference Engine
+// Architecture?", Tensor Parallelism Optimization, item 3) without a format;
+// the format here is OCP FP8 E4M3 with one fp32 scale per pool: a value x is
+// stored as the code nearest to clamp(x * (1/s), -448, 448) (ties to even, the
+// hardware converter's rounding) and read back as code * s.
+//
+// Decode works per (sequence, 256-token block, group of GT query heads of one
+// KV head): one workgroup streams that block's K and V rows (128 bytes per
+// row and head at D = 128) and leaves an online-softmax partial (max, sum,
+// unnormalised output) in the workspace; a second kernel merges a sequence's
+// block partials in block order (deterministic, no atomics) and writes the
+// bf16 output. Inside a workgroup each wave takes 64 rows of the block: 8 lane
+// groups of 8 lanes, a lane holding 16 consecutive dims of a row, with all 8
+// of its rows' K and V loads issued before any arithmetic. q.k sums over the
+// 8 lanes of a group by xor shuffles; the 8 groups of a wave and then the 4
+// waves merge their softmax states at the end.
+#include <math.h>
+
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kF8Threads = 256;
+constexpr int kF8Waves = kF8Threads / kWave;
+constexpr int kF8D = 128;                       // head dim supported
+constexpr int kF8RowsPerWave = kTokensPerBlock / kF8Waves;  // 64
+constexpr int kF8Iters = kF8RowsPerWave / 8;    // rows per lane group
+constexpr float kF8Empty = -1.0e30f;            // running max before any row
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Four fp8 codes (one word) to four floats (exact).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
+  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+  o[0] = lo[0];
+  o[1] = lo[1];
+  o[2] = hi[0];
+  o[3] = hi[1];
+}
+
+__device__ __forceinline__ float clamp_fp8(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
+
+// Quantising store: one thread per 8 elements of a token's [Hkv, D] row of K
+// and the same of V.
+__global__ __launch_bounds__(256) void kv_store_fp8_kernel(uint8_t* __restrict__ k_cache,
+                                                          uint8_t* __restrict__ v_cache,
+                                                          const u32x4_t* __restrict__ k,
+                                                          const u32x4_t* __restrict__ v,
+                                                          const int32_t* __restrict__ slot_mapping,
+                                                          int64_t total_pieces, int32_t pieces_per_row, float inv_k,
+                                                          float inv_v) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total_pieces) return;
+  const int64_t token = i / pieces_per_row;
+  const int32_t piece = static_cast<int32_t>(i - token * pieces_per_row);
+  const int32_t slot = slot_mapping[token];
+  const u32x4_t kk = __builtin_nontemporal_load(k + i);
+  const u32x4_t vv = __builtin_nontemporal_load(v + i);
+  if (slot < 0) return;
+  uint32_t kw[2], vw[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    // bf16 words 2h and 2h+1 hold elements 4h .. 4h+3
+    int wk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fp8(bf16_lo(kk[2 * h]) * inv_k),
+                                             clamp_fp8(bf16_hi(kk[2 * h]) * inv_k), 0, false);
+    wk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fp8(bf16_lo(kk[2 * h + 1]) * inv_k),
+                                         clamp_fp8(bf16_hi(kk[2 * h + 1]) * inv_k), wk, true);
+    int wv = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fp8(bf16_lo(vv[2 * h]) * inv_v),
+                                             clamp_fp8(bf16_hi(vv[2 * h]) * inv_v), 0, false);
+    wv = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fp8(bf16_lo(vv[2 * h + 1]) * inv_v),
+                                         clamp_fp8(bf16_hi(vv[2 * h + 1]) * inv_v), wv, true);
+    kw[h] = static_cast<uint32_t>(wk);
+    vw[h] = static_cast<uint32_t>(wv);
+  }
+  const int64_t dst = (static_cast<int64_t>(slot) * pieces_per_row + piece) * 8;
+  uint2 ko, vo;
+  ko.x = kw[0];
+  ko.y = kw[1];
+  vo.x = vw[0];
+  vo.y = vw[1];
+  *reinterpret_cast<uint2*>(k_cache + dst) = ko;
+  *reinterpret_cast<uint2*>(v_cache + dst) = vo;
+}
+
+template <int GT>
+__global__ __launch_bounds__(kF8Threads) void decode_fp8_block_kernel(DecodeFp8Args a) {
+  __shared__ float s_m[kF8Waves][GT];
+  __shared__ float s_l[kF8Waves][GT];
+  __shared__ float s_acc[kF8Waves][GT][kF8D];
+  const int HG = a.num_q_heads / GT;
+  int item = blockIdx.x;
+  const int hg = item % HG;
+  item /= HG;
+  const int b = item % a.max_blocks;
+  const int seq = item / a.max_blocks;
+  const int ctx = min(max(a.context_lens[seq], 0), a.max_context_len);
+  const int t0 = b * kTokensPerBlock;
+  if (t0 >= ctx) return;  // the whole workgroup: past this sequence's context
+  const int nrows = min(kTokensPerBlock, ctx - t0);
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int hq0 = hg * GT;
+  const int kvh = hq0 / group;
+  const int blk = a.block_tables[static_cast<int64_t>(seq) * a.max_blocks_per_seq + b];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int grp = lane >> 3;  // lane group: one row at a time
+  const int sl = lane & 7;    // dims [16 sl, 16 sl + 16)
+
+  // all of this lane's K and V rows first
+  const int64_t row_stride = static_cast<int64_t>(a.num_kv_heads) * kF8D;
+  const uint8_t* kb = static_cast<const uint8_t*>(a.k_cache) +
+                      (static_cast<int64_t>(blk) * kTokensPerBlock) * row_stride + kvh * kF8D + sl * 16;
+  const uint8_t* vb = static_cast<const uint8_t*>(a.v_cache) +
+                      (static_cast<int64_t>(blk) * kTokensPerBlock) * row_stride + kvh * kF8D + sl * 16;
+  u32x4_t kr[kF8Iters], vr[kF8Iters];
+#pragma unroll
+  for (int it = 0; it < kF8Iters; ++it) {
+    const int r = min(wave * kF8RowsPerWave + it * 8 + grp, nrows - 1);  // past the context: re-read a row
+    kr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + r * row_stride));
+    vr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + r * row_stride));
+  }
+  // the lane's 16 query dims of each head, fp32
+  float qf[GT][16];
+  const uint32_t* qw = static_cast<const uint32_t*>(a.q);
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    const int64_t base = ((static_cast<int64_t>(seq) * a.num_q_heads + hq0 + g) * kF8D + sl * 16) / 2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t x = qw[base + j];
+      qf[g][2 * j] = bf16_lo(x);
+      qf[g][2 * j + 1] = bf16_hi(x);
+    }
+  }
+
+  float m[GT], l[GT], acc[GT][16];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    m[g] = kF8Empty;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[g][e] = 0.0f;
+  }
+  const float sc = a.scale_log2;
+#pragma unroll
+  for (int it = 0; it < kF8Iters; ++it) {
+    const bool valid = wave * kF8RowsPerWave + it * 8 + grp < nrows;
+    float kf[16], vf[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      fp8x4_to_f32(kr[it][w], kf + 4 * w);
+      fp8x4_to_f32(vr[it][w], vf + 4 * w);
+    }
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s = fmaf(qf[g][e], kf[e], s);
+      s += __shfl_xor(s, 1, kWave);
+      s += __shfl_xor(s, 2, kWave);
+      s += __shfl_xor(s, 4, kWave);
+      if (valid) {
+        const float s2 = s * sc;
+        const float mn = fmaxf(m[g], s2);
+        const float corr = exp2_fast(m[g] - mn);
+        const float p = exp2_fast(s2 - mn);
+        l[g] = l[g] * corr + p;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e] * corr);
+        m[g] = mn;
+      }
+    }
+  }
+  // merge the 8 lane groups of the wave (lanes with the same dims differ in bits 3..5)
+#pragma unroll
+  for (int off = 8; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const float mo = __shfl_xor(m[g], off, kWave);
+      const float lo = __shfl_xor(l[g], off, kWave);
+      const float mn = fmaxf(m[g], mo);
+      const float ca = exp2_fast(m[g] - mn);
+      const float cb = exp2_fast(mo - mn);
+      l[g] = l[g] * ca + lo * cb;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float ao = __shfl_xor(acc[g][e], off, kWave);
+        acc[g][e] = acc[g][e] * ca + ao * cb;
+      }
+      m[g] = mn;
+    }
+  }
+  if (lane < 8) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      if (lane == 0) {
+        s_m[wave][g] = m[g];
+        s_l[wave][g] = l[g];
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s_acc[wave][g][sl * 16 + e] = acc[g][e];
+    }
+  }
+  __syncthreads();
+  // the block's partial for each head: threads 0..127 take one dim each
+  if (tid < kF8D) {
+    const int64_t prow = (static_cast<int64_t>(seq) * a.max_blocks + b) * a.num_q_heads + hq0;
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float mm = kF8Empty;
+#pragma unroll
+      for (int w = 0; w < kF8Waves; ++w) mm = fmaxf(mm, s_m[w][g]);
+      float ll = 0.0f, aa = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kF8Waves; ++w) {
+        const float c = exp2_fast(s_m[w][g] - mm);
+        ll = fmaf(s_l[w][g], c, ll);
+        aa = fmaf(s_acc[w][g][tid], c, aa);
+      }
+      a.part_acc[(prow + g) * kF8D + tid] = aa;
+      if (tid == 0) {
+        a.part_ml[2 * (prow + g)] = mm;
+        a.part_ml[2 * (prow + g) + 1] = ll;
+      }
+    }
+  }
+}
+
+// Merges a sequence's block partials (in block order) into the bf16 output.
+__global__ __launch_bounds__(kF8D) void decode_fp8_merge_kernel(DecodeFp8Args a) {
+  const int seq = blockIdx.x / a.num_q_heads;
+  const int hq = blockIdx.x % a.num_q_heads;
+  const int d = threadIdx.x;
+  const int ctx = min(max(a.context_lens[seq], 0), a.max_context_len);
+  const int nb = (ctx + kTokensPerBlock - 1) / kTokensPerBlock;
+  if (nb == 0) return;  // empty context: the row stays unwritten
+  float mm = kF8Empty, ll = 0.0f, aa = 0.0f;
+  for (int b = 0; b < nb; ++b) {
+    const int64_t prow = (static_cast<int64_t>(seq) * a.max_blocks + b) * a.num_q_heads + hq;
+    const float mb = a.part_ml[2 * prow];
+    const float lb = a.part_ml[2 * prow + 1];
+    const float ab = a.part_acc[prow * kF8D + d];
+    const float mn = fmaxf(mm, mb);
+    const float ca = exp2_fast(mm - mn);
+    const float cb = exp2_fast(mb - mn);
+    ll = ll * ca + lb * cb;
+    aa = aa * ca + ab * cb;
+    mm = mn;
+  }
+  bf16_t* out = static_cast<bf16_t*>(a.out);
+  out[(static_cast<int64_t>(seq) * a.num_q_heads + hq) * kF8D + d].bits = to_bf16_bits(aa / ll * a.v_scale);
+}
+
+}  // namespace
+
+hipError_t launch_kv_store_fp8(void* k_cache, void* v_cache, const void* k, const void* v,
+                               const int32_t* slot_mapping, int32_t num_tokens, int32_t row_elems, float inv_k,
+                               float inv_v, hipStream_t stream) {
+  const int32_t pieces_per_row = row_elems / 8;
+  const int64_t total = static_cast<int64_t>(num_tokens) * pieces_per_row;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  kv_store_fp8_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream>>>(
+      static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), static_cast<const u32x4_t*>(k),
+      static_cast<const u32x4_t*>(v), slot_mapping, total, pieces_per_row, inv_k, inv_v);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_fp8(const DecodeFp8Args& a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int gt = decode_head_group(group);
+  const int64_t items = static_cast<int64_t>(a.num_seqs) * a.max_blocks * (a.num_q_heads / gt);
+  if (items == 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>(items)), block(kF8Threads);
+  if (gt == 4)
+    decode_fp8_block_kernel<4><<<grid, block, 0, stream>>>(a);
+  else if (gt == 2)
+    decode_fp8_block_kernel<2><<<grid, block, 0, stream>>>(a);
+  else
+    decode_fp8_block_kernel<1><<<grid, block, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_fp8_merge_kernel<<<dim3(static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * a.num_q_heads)),
+                            dim3(kF8D), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -60,6 +60,33 @@ constexpr int32_t kDecodeMaxGroup = 4;  // query heads per decode workgroup
 
 hipError_t launch_decode(const DecodeArgs& args, Dtype dtype, int32_t head_dim, hipStream_t stream);
 
+// fp8 (E4M3) KV cache: quantising store and decode.
+hipError_t launch_kv_store_fp8(void* k_cache, void* v_cache, const void* k, const void* v,
+                               const int32_t* slot_mapping, int32_t num_tokens, int32_t row_elems, float inv_k,
+                               float inv_v, hipStream_t stream);
+
+struct DecodeFp8Args {
+  void* out;  // bf16 [num_seqs, num_q_heads, 128]
+  const void* q;
+  const void* k_cache;  // fp8 codes [num_blocks, 256, num_kv_heads, 128]
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks_per_seq;
+  int32_t max_context_len;
+  int32_t max_blocks;  // ceil(max_context_len / 256): block partials per sequence
+  float scale_log2;    // scale * k_scale * log2(e)
+  float v_scale;
+  float* part_ml;   // [num_seqs][max_blocks][num_q_heads][2]: running max (log2 units) and sum
+  float* part_acc;  // [num_seqs][max_blocks][num_q_heads][128]: unnormalised outputs
+};
+
+hipError_t launch_decode_fp8(const DecodeFp8Args& args, hipStream_t stream);
+
+
 // Grid the decode launcher uses when the caller does not fix one.
 int decode_default_workgroups(Dtype dtype, int32_t head_dim, int32_t group, int64_t max_units);
 
@@ -131,6 +158,17 @@ inline WorkspaceLayout make_workspace_layout(int64_t slot_rows, int64_t counters
   w.out_off = static_cast<size_t>((slot_rows * 4 + 255) / 256 * 256);
   w.counters_off = w.out_off + static_cast<size_t>(slot_rows * kMaxHeadDim * 4);
   w.total = w.counters_off + static_cast<size_t>(counters * 4);
+  return w;
+}
+
+// Workspace of the fp8 decode: every (sequence, block, query head) partial.
+inline WorkspaceLayout decode_fp8_workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t max_blocks) {
+  WorkspaceLayout w;
+  const int64_t rows = num_seqs * max_blocks * num_q_heads;
+  w.lse_off = 0;
+  w.out_off = static_cast<size_t>((rows * 2 * 4 + 255) / 256 * 256);
+  w.counters_off = w.out_off + static_cast<size_t>(rows * 128 * 4);
+  w.total = w.counters_off;
   return w;
 }
 

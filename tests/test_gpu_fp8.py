@@ -1,0 +1,98 @@
+"""fp8 KV cache on the GPU against the oracle (oracle/fp8_kv.py): the
+quantising store bit for bit (including saturating and subnormal values and
+skipped slots), and decode attention over fp8 pools within the bf16 bar for
+GQA groups 1, 2 and 4, ragged contexts, NaN codes in every row no context
+covers, the Qwen3-0.6B-shaped decode workload at full size, and repeated runs
+bit-identical."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.fp8_kv as f8
+import paged_kv_cache_209_amd as pa
+import workloads as w
+from gpu_util import DEV, compare, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_store_bit_exact():
+    say("fp8 store")
+    g = torch.Generator().manual_seed(8)
+    rng = np.random.default_rng(8)
+    t, hkv, d, nb = 300, 8, 128, 6
+    k = torch.randn(t, hkv, d, generator=g)
+    v = torch.randn(t, hkv, d, generator=g)
+    k[::7] *= 1000.0   # saturates at +-448 codes
+    v[1::9] *= 1e-4    # subnormal codes
+    k, v = k.to(torch.bfloat16), v.to(torch.bfloat16)
+    kc = torch.randint(0, 256, (nb, 256, hkv, d), generator=g, dtype=torch.uint8)
+    vc = torch.randint(0, 256, (nb, 256, hkv, d), generator=g, dtype=torch.uint8)
+    slots = torch.from_numpy(rng.permutation(nb * 256)[:t].astype(np.int32))
+    slots[2::5] = -1
+    ks, vs = 0.05, 0.02
+    ref_k, ref_v = f8.kv_store_fp8(kc, vc, k, v, slots, ks, vs)
+    dkc, dvc = to_dev(kc), to_dev(vc)
+    pa.kv_store_fp8(dkc, dvc, to_dev(k), to_dev(v), to_dev(slots), ks, vs)
+    torch.cuda.synchronize()
+    assert torch.equal(dkc.cpu(), ref_k)
+    assert torch.equal(dvc.cpu(), ref_v)
+
+
+def fp8_case(seed, ctx, hq, hkv, scales=(0.0125, 0.0125), poison=True):
+    c = w.build_decode_case(f"fp8_{seed}", ctx, hq, hkv, 128, torch.bfloat16, seed)
+    kq = f8.quantize(c.k_cache, scales[0])
+    vq = f8.quantize(c.v_cache, scales[1])
+    if poison:
+        cov = w.covered_rows(c.block_tables, c.context_lens, c.num_blocks)
+        kq = kq.clone()
+        vq = vq.clone()
+        kq[~cov] = 0x7F  # NaN codes wherever no context reads
+        vq[~cov] = 0x7F
+    return c, kq, vq
+
+
+def run(c, kq, vq, scales):
+    q = to_dev(c.q)
+    out = torch.empty_like(q)
+    pa.paged_attn_decode_fp8(out, q, to_dev(kq), to_dev(vq), to_dev(c.block_tables), to_dev(c.context_lens),
+                             c.scale, scales[0], scales[1], c.max_context_len)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8)], ids=["g1", "g2", "g4"])
+def test_decode_matches_oracle(hq, hkv):
+    say(f"fp8 decode hq={hq} hkv={hkv}")
+    scales = (0.0125, 0.02)
+    c, kq, vq = fp8_case(3 + hq, [1, 37, 256, 257, 513, 1000, 2048], hq, hkv, scales)
+    out = run(c, kq, vq, scales)
+    ref = f8.paged_attn_decode_fp8(c.q, kq, vq, c.block_tables, c.context_lens, c.scale, *scales)
+    compare(out, ref, torch.bfloat16)
+    again = run(c, kq, vq, scales)
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+
+
+def test_one_token_context_returns_dequantised_v():
+    scales = (0.0125, 0.02)
+    c, kq, vq = fp8_case(41, [1, 1, 300], 16, 8, scales)
+    out = run(c, kq, vq, scales).cpu()
+    for i in (0, 1):
+        blk = int(c.block_tables[i, 0])
+        want = f8.dequantize(vq[blk, 0], scales[1])  # [Hkv, D]
+        for g in range(16):
+            assert torch.equal(out[i, g], want[g // 2].to(torch.float32).to(torch.bfloat16))
+
+
+def test_qwen3_0_6b_decode_workload_full_size():
+    """Batch 64, 16 Q / 8 KV heads, contexts U[128, 4096], the pools of the
+    bf16 workload quantised with scale 1/80."""
+    say("fp8 decode c2 full size")
+    c = w.config2()
+    s = 1.0 / 80.0
+    kq, vq = f8.quantize(c.k_cache, s), f8.quantize(c.v_cache, s)
+    out = run(c, kq, vq, (s, s))
+    seqs = list(range(0, 64, 3))
+    ref = f8.paged_attn_decode_fp8(c.q, kq, vq, c.block_tables, c.context_lens, c.scale, s, s, seqs=seqs)
+    compare(out, ref, torch.bfloat16, rows=seqs)
