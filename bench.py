@@ -284,6 +284,52 @@ def run_rope_store(torch, pa, w, steps):
             "rope_theta": ROPE_THETA}
 
 
+FP8_SCALE = 1.0 / 80.0  # per-pool scale: N(0,1) values stay far inside the +-448 code range
+
+
+def run_fp8_decode(torch, pa, case, steps, copies):
+    """Decode over fp8 (E4M3) copies of the workload's pools: the bf16 pools
+    are quantised on the GPU by pa_kv_store_fp8 (every slot), then `steps`
+    back-to-back fp8 decode launches on rotating copies are timed with one
+    event pair. Algorithmic bytes: the fp8 K and V rows of every context once
+    (shared rows once), bf16 q and out, block-table entries and lengths."""
+    dev = "cuda:0"
+    nb, bs, hkv, d = case.k_cache.shape
+    slots = torch.arange(nb * bs, dtype=torch.int32, device=dev)
+    kq = torch.empty((nb, bs, hkv, d), dtype=torch.uint8, device=dev)
+    vq = torch.empty_like(kq)
+    pa.kv_store_fp8(kq, vq, case.k_cache.to(dev).reshape(nb * bs, hkv, d), case.v_cache.to(dev).reshape(nb * bs, hkv, d),
+                    slots, FP8_SCALE, FP8_SCALE)
+    kqs, vqs = [kq], [vq]
+    for _ in range(copies - 1):
+        kqs.append(kq.clone())
+        vqs.append(vq.clone())
+    q = case.q.to(dev)
+    out = torch.empty_like(q)
+    bt, cl = case.block_tables.to(dev), case.context_lens.to(dev)
+    maxc = case.max_context_len
+    ws = torch.empty(pa.decode_fp8_workspace_bytes(case.num_seqs, case.num_q_heads, d, maxc), dtype=torch.uint8,
+                     device=dev)
+
+    def decode(i):
+        pa.paged_attn_decode_fp8(out, q, kqs[i % copies], vqs[i % copies], bt, cl, case.scale, FP8_SCALE, FP8_SCALE,
+                                 maxc, workspace_tensor=ws)
+
+    for i in range(3):
+        decode(i)
+    ms = time_launches(torch, decode, steps)
+    db = decode_bytes(case)
+    kv_fp8 = db["unique_kv"] // case.q.element_size()  # one byte per element instead of two
+    nbytes = db["total"] - db["unique_kv"] + kv_fp8
+    del kqs, vqs, kq, vq
+    torch.cuda.empty_cache()
+    return {"decode_avg_us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+            "TBps": round(nbytes / (ms * 1e-3) / 1e12, 4),
+            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "context_tokens_per_s": round(int(case.context_lens.sum()) / (ms * 1e-3), 1),
+            "scale": FP8_SCALE, "pool_copies_rotated": copies}
+
+
 def run_decode_graphs(torch, pa, steps):
     """Decode steps (store of the new tokens + paged decode) issued eagerly
     (two binding calls per step, exact max context) and as one graph launch
@@ -458,7 +504,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-secondary", action="store_true")
-    ap.add_argument("--only", default="", help="run just one workload: c2 | c4 | c3 | rope | c5 | graphs | bm (profiling)")
+    ap.add_argument("--only", default="", help="run just one workload: c2 | c4 | c3 | rope | c5 | fp8 | graphs | bm (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy --steps times (counter calibration)")
     args = ap.parse_args()
@@ -589,6 +635,16 @@ def main():
         }
         del c5
         torch.cuda.empty_cache()
+    if not args.skip_secondary and args.only in ("", "fp8"):
+        c2f = w.config2(device="cuda:0")
+        fp8 = {"c2_qwen3_0.6b": run_fp8_decode(torch, pa, c2f, max(20, args.steps), args.copies)}
+        del c2f
+        torch.cuda.empty_cache()
+        c4f = w.config4(device="cuda:0")
+        fp8["c4_qwen3_8b_shared_prefix"] = run_fp8_decode(torch, pa, c4f, max(5, args.steps // 5), 1)
+        del c4f
+        torch.cuda.empty_cache()
+        secondary["fp8_kv_decode"] = fp8
     if not args.skip_secondary and args.only in ("", "graphs"):
         secondary["decode_step_graphs_vs_eager"] = run_decode_graphs(torch, pa, max(50, args.steps))
     if not args.skip_secondary and args.only in ("", "bm"):

@@ -14,8 +14,8 @@
 // bf16 output. Inside a workgroup each wave takes 64 rows of the block: 8 lane
 // groups of 8 lanes, a lane holding 16 consecutive dims of a row, with all 8
 // of its rows' K and V loads issued before any arithmetic. q.k sums over the
-// 8 lanes of a group by xor shuffles; the 8 groups of a wave and then the 4
-// waves merge their softmax states at the end.
+// 8 lanes of a group by DPP; the 8 groups of a wave merge their softmax states
+// by a DPP row rotate and the gfx950 permlane swaps, the 4 waves through LDS.
 #include <math.h>
 
 #include "pa_device.h"
@@ -163,9 +163,7 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_block_kernel(DecodeFp8A
       float s = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) s = fmaf(qf[g][e], kf[e], s);
-      s += __shfl_xor(s, 1, kWave);
-      s += __shfl_xor(s, 2, kWave);
-      s += __shfl_xor(s, 4, kWave);
+      s = sum8(s);  // the row's 8 lanes, by DPP
       if (valid) {
         const float s2 = s * sc;
         const float mn = fmaxf(m[g], s2);
@@ -178,21 +176,40 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_block_kernel(DecodeFp8A
       }
     }
   }
-  // merge the 8 lane groups of the wave (lanes with the same dims differ in bits 3..5)
+  // merge the 8 lane groups of the wave (lanes with the same dims differ in
+  // bits 3..5): the bit-3 partner by a DPP row rotate, bits 4 and 5 by the
+  // gfx950 permlane swaps (no LDS traffic). Both lanes of a pair form the same
+  // merged state from the same two inputs.
 #pragma unroll
-  for (int off = 8; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const float mo = __shfl_xor(m[g], off, kWave);
-      const float lo = __shfl_xor(l[g], off, kWave);
-      const float mn = fmaxf(m[g], mo);
-      const float ca = exp2_fast(m[g] - mn);
-      const float cb = exp2_fast(mo - mn);
-      l[g] = l[g] * ca + lo * cb;
+  for (int g = 0; g < GT; ++g) {
+    {
+      const float mo = dpp_f32<kDppRowRor8>(m[g]);
+      const float lo = dpp_f32<kDppRowRor8>(l[g]);
+      const bool upper = (lane & 8) != 0;
+      const float m_lo = upper ? mo : m[g], m_hi = upper ? m[g] : mo;
+      const float l_lo = upper ? lo : l[g], l_hi = upper ? l[g] : lo;
+      const float mn = fmaxf(m_lo, m_hi);
+      const float ca = exp2_fast(m_lo - mn), cb = exp2_fast(m_hi - mn);
+      l[g] = l_lo * ca + l_hi * cb;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float ao = __shfl_xor(acc[g][e], off, kWave);
-        acc[g][e] = acc[g][e] * ca + ao * cb;
+        const float ao = dpp_f32<kDppRowRor8>(acc[g][e]);
+        const float a_lo = upper ? ao : acc[g][e], a_hi = upper ? acc[g][e] : ao;
+        acc[g][e] = a_lo * ca + a_hi * cb;
+      }
+      m[g] = mn;
+    }
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+      const LanePair mp = step == 0 ? pair_across_rows(m[g]) : pair_across_halves(m[g]);
+      const LanePair lp = step == 0 ? pair_across_rows(l[g]) : pair_across_halves(l[g]);
+      const float mn = fmaxf(mp.lo, mp.hi);
+      const float ca = exp2_fast(mp.lo - mn), cb = exp2_fast(mp.hi - mn);
+      l[g] = lp.lo * ca + lp.hi * cb;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const LanePair ap = step == 0 ? pair_across_rows(acc[g][e]) : pair_across_halves(acc[g][e]);
+        acc[g][e] = ap.lo * ca + ap.hi * cb;
       }
       m[g] = mn;
     }

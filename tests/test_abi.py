@@ -185,3 +185,38 @@ def test_decode_graphs_validation():
     assert lib.pa_decode_graphs_launch(None, 1, None) == INVALID
     assert lib.pa_decode_graphs_bucket(None, 1) == 0
     lib.pa_decode_graphs_destroy(None)
+
+
+def test_fp8_validation():
+    lib = pa.library()
+
+    def store(**kw):
+        a = dict(kc=P, vc=P, k=P, v=P, slots=P, T=4, hkv=2, d=128, bs=256, nb=8, ks=0.1, vs=0.1)
+        a.update(kw)
+        return lib.pa_kv_store_fp8(a["kc"], a["vc"], a["k"], a["v"], a["slots"], a["T"], a["hkv"], a["d"], a["bs"],
+                                   a["nb"], a["ks"], a["vs"], None)
+
+    assert store(kc=None) == INVALID
+    assert store(d=64) == UNSUP
+    assert store(ks=0.0) == INVALID and store(vs=-1.0) == INVALID and store(ks=float("inf")) == INVALID
+    assert store(T=0, k=None) == pa.PA_OK
+    assert store(k=P + 4) == INVALID
+
+    def dec(**kw):
+        a = dict(out=P, q=P, kc=P, vc=P, bt=P, cl=P, B=2, hq=8, hkv=2, d=128, bs=256, nb=8, mb=4, mc=1000,
+                 scale=0.1, ks=0.1, vs=0.1, ws=P, wsb=1 << 30)
+        a.update(kw)
+        return lib.pa_paged_attn_decode_fp8(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["B"], a["hq"],
+                                            a["hkv"], a["d"], a["bs"], a["nb"], a["mb"], a["mc"], a["scale"], a["ks"],
+                                            a["vs"], a["ws"], a["wsb"], None)
+
+    assert dec(d=64) == UNSUP
+    assert dec(hq=6, hkv=4) == INVALID
+    assert dec(mc=4 * 256 + 1) == INVALID
+    assert dec(ks=0.0) == INVALID
+    assert dec(ws=None) == WS
+    assert dec(wsb=16) == WS
+    assert dec(B=0, out=None) == pa.PA_OK
+    need = pa.decode_fp8_workspace_bytes(2, 8, 128, 1000)
+    assert need == pa.decode_fp8_workspace_bytes(2, 8, 128, 1024) > 0
+    assert pa.decode_fp8_workspace_bytes(2, 8, 64, 1000) == 0
