@@ -251,8 +251,12 @@ pa_status pa_paged_attn_decode_fp8(void* out, const void* q, const void* k_cache
   if (num_seqs == 0) return PA_OK;
   if (out == nullptr || q == nullptr || block_tables == nullptr || context_lens == nullptr) return PA_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID_ARG;
-  const int32_t max_blocks = static_cast<int32_t>(ceil_div(max_context_len, kBlockSize));
+  // the workspace holds one-block chunks, the most partials any call uses
+  const int64_t max_blocks = ceil_div(max_context_len, kBlockSize);
   const pa::WorkspaceLayout lay = pa::decode_fp8_workspace_layout(num_seqs, num_q_heads, max_blocks);
+  const int32_t bpc = pa::fp8_blocks_per_chunk(num_seqs, num_q_heads / pa::decode_head_group(num_q_heads / num_kv_heads),
+                                               max_blocks);
+  const int32_t max_chunks = static_cast<int32_t>(ceil_div(max_blocks, bpc));
   if (workspace == nullptr || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
   pa::DecodeFp8Args a;
@@ -267,7 +271,8 @@ pa_status pa_paged_attn_decode_fp8(void* out, const void* q, const void* k_cache
   a.num_kv_heads = num_kv_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
-  a.max_blocks = max_blocks;
+  a.blocks_per_chunk = bpc;
+  a.max_chunks = max_chunks;
   a.scale_log2 = scale * k_scale * kLog2e;
   a.v_scale = v_scale;
   char* ws = static_cast<char*>(workspace);

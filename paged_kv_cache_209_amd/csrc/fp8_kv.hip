@@ -6,14 +6,15 @@
 // stored as the code nearest to clamp(x * (1/s), -448, 448) (ties to even, the
 // hardware converter's rounding) and read back as code * s.
 //
-// Decode works per (sequence, 256-token block, group of GT query heads of one
-// KV head): one workgroup streams that block's K and V rows (128 bytes per
-// row and head at D = 128) and leaves an online-softmax partial (max, sum,
-// unnormalised output) in the workspace; a second kernel merges a sequence's
-// block partials in block order (deterministic, no atomics) and writes the
-// bf16 output. Inside a workgroup each wave takes 64 rows of the block: 8 lane
-// groups of 8 lanes, a lane holding 16 consecutive dims of a row, with all 8
-// of its rows' K and V loads issued before any arithmetic. q.k sums over the
+// Decode works per (sequence, chunk of 1, 2 or 4 256-token blocks, group of GT
+// query heads of one KV head): one workgroup streams the chunk's K and V rows (128
+// bytes per row and head at D = 128) block by block and leaves an
+// online-softmax partial (reference max, sum, unnormalised output) in the
+// workspace; a second kernel merges a sequence's chunk partials in order
+// (deterministic, no atomics) and writes the bf16 output. Inside a workgroup
+// each wave takes 64 rows of each block: 8 lane groups of 8 lanes, a lane
+// holding 16 consecutive dims of a row, with all 8 of its rows' K and V loads
+// of a block issued before any arithmetic on them. q.k sums over the
 // 8 lanes of a group by DPP; the 8 groups of a wave merge their softmax states
 // by a DPP row rotate and the gfx950 permlane swaps, the 4 waves through LDS.
 #include <math.h>
@@ -31,17 +32,13 @@ constexpr int kF8D = 128;                       // head dim supported
 constexpr int kF8RowsPerWave = kTokensPerBlock / kF8Waves;  // 64
 constexpr int kF8Iters = kF8RowsPerWave / 8;    // rows per lane group
 constexpr float kF8Empty = -1.0e30f;            // running max before any row
+constexpr float kF8Slack = 8.0f;                // log2 units the reference max may lag by
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Four fp8 codes (one word) to four floats (exact).
-__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
-  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
-  o[0] = lo[0];
-  o[1] = lo[1];
-  o[2] = hi[0];
-  o[3] = hi[1];
+// Two fp8 codes (the low or the high half of a word) to a bf16 pair (exact:
+// every E4M3 value is a bf16 value), the first code in the low half.
+template <bool kHigh>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
 }
 
 __device__ __forceinline__ float clamp_fp8(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
@@ -97,47 +94,31 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_block_kernel(DecodeFp8A
   int item = blockIdx.x;
   const int hg = item % HG;
   item /= HG;
-  const int b = item % a.max_blocks;
-  const int seq = item / a.max_blocks;
+  const int chunk = item % a.max_chunks;
+  const int seq = item / a.max_chunks;
   const int ctx = min(max(a.context_lens[seq], 0), a.max_context_len);
-  const int t0 = b * kTokensPerBlock;
-  if (t0 >= ctx) return;  // the whole workgroup: past this sequence's context
-  const int nrows = min(kTokensPerBlock, ctx - t0);
+  const int nb_ctx = (ctx + kTokensPerBlock - 1) / kTokensPerBlock;
+  const int b_begin = chunk * a.blocks_per_chunk;
+  if (b_begin >= nb_ctx) return;  // the whole workgroup: past this sequence's context
+  const int b_end = min(b_begin + a.blocks_per_chunk, nb_ctx);
   const int group = a.num_q_heads / a.num_kv_heads;
   const int hq0 = hg * GT;
   const int kvh = hq0 / group;
-  const int blk = a.block_tables[static_cast<int64_t>(seq) * a.max_blocks_per_seq + b];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int grp = lane >> 3;  // lane group: one row at a time
   const int sl = lane & 7;    // dims [16 sl, 16 sl + 16)
-
-  // all of this lane's K and V rows first
   const int64_t row_stride = static_cast<int64_t>(a.num_kv_heads) * kF8D;
-  const uint8_t* kb = static_cast<const uint8_t*>(a.k_cache) +
-                      (static_cast<int64_t>(blk) * kTokensPerBlock) * row_stride + kvh * kF8D + sl * 16;
-  const uint8_t* vb = static_cast<const uint8_t*>(a.v_cache) +
-                      (static_cast<int64_t>(blk) * kTokensPerBlock) * row_stride + kvh * kF8D + sl * 16;
-  u32x4_t kr[kF8Iters], vr[kF8Iters];
-#pragma unroll
-  for (int it = 0; it < kF8Iters; ++it) {
-    const int r = min(wave * kF8RowsPerWave + it * 8 + grp, nrows - 1);  // past the context: re-read a row
-    kr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + r * row_stride));
-    vr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + r * row_stride));
-  }
-  // the lane's 16 query dims of each head, fp32
-  float qf[GT][16];
+
+  // the lane's 16 query dims of each head, as 8 bf16 pairs
+  uint32_t qp[GT][8];
   const uint32_t* qw = static_cast<const uint32_t*>(a.q);
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
     const int64_t base = ((static_cast<int64_t>(seq) * a.num_q_heads + hq0 + g) * kF8D + sl * 16) / 2;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t x = qw[base + j];
-      qf[g][2 * j] = bf16_lo(x);
-      qf[g][2 * j + 1] = bf16_hi(x);
-    }
+    for (int j = 0; j < 8; ++j) qp[g][j] = qw[base + j];
   }
 
   float m[GT], l[GT], acc[GT][16];
@@ -149,33 +130,77 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_block_kernel(DecodeFp8A
     for (int e = 0; e < 16; ++e) acc[g][e] = 0.0f;
   }
   const float sc = a.scale_log2;
+  for (int b = b_begin; b < b_end; ++b) {
+  const int nrows = min(kTokensPerBlock, ctx - b * kTokensPerBlock);
+  const int blk = a.block_tables[static_cast<int64_t>(seq) * a.max_blocks_per_seq + b];
+  // all of this lane's K and V rows of the block first
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache) +
+                         (static_cast<int64_t>(blk) * kTokensPerBlock) * row_stride + kvh * kF8D + sl * 16;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache) +
+                         (static_cast<int64_t>(blk) * kTokensPerBlock) * row_stride + kvh * kF8D + sl * 16;
+  u32x4_t kr[kF8Iters], vr[kF8Iters];
 #pragma unroll
   for (int it = 0; it < kF8Iters; ++it) {
-    const bool valid = wave * kF8RowsPerWave + it * 8 + grp < nrows;
-    float kf[16], vf[16];
+    const int r = min(wave * kF8RowsPerWave + it * 8 + grp, nrows - 1);  // past the context: re-read a row
+    kr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kbase + r * row_stride));
+    vr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vbase + r * row_stride));
+  }
+  // Two rows (a, b) per step: codes become bf16 pairs (exact), q.k is 8
+  // v_dot2_f32_bf16 per row, and p.V pairs the two rows in one v_dot2 per dim
+  // (p rounded to bf16, the sum l taken from the same rounded p). m is a
+  // reference, not necessarily the running max: l and acc are relative to it,
+  // which every later merge respects.
+#pragma unroll
+  for (int it = 0; it < kF8Iters; it += 2) {
+    const int ra = wave * kF8RowsPerWave + it * 8 + grp;
+    const bool a_ok = ra < nrows, b_ok = ra + 8 < nrows;
+    uint32_t ka[8], kb[8], vl[8], vh[8];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      fp8x4_to_f32(kr[it][w], kf + 4 * w);
-      fp8x4_to_f32(vr[it][w], vf + 4 * w);
+      ka[2 * w] = fp8x2_to_bf16x2<false>(kr[it][w]);
+      ka[2 * w + 1] = fp8x2_to_bf16x2<true>(kr[it][w]);
+      kb[2 * w] = fp8x2_to_bf16x2<false>(kr[it + 1][w]);
+      kb[2 * w + 1] = fp8x2_to_bf16x2<true>(kr[it + 1][w]);
+      const uint32_t va0 = fp8x2_to_bf16x2<false>(vr[it][w]), va1 = fp8x2_to_bf16x2<true>(vr[it][w]);
+      const uint32_t vb0 = fp8x2_to_bf16x2<false>(vr[it + 1][w]), vb1 = fp8x2_to_bf16x2<true>(vr[it + 1][w]);
+      // (v_a[e], v_b[e]) for dims e = 4w .. 4w+3
+      vl[2 * w] = pair_lo(va0, vb0);
+      vh[2 * w] = pair_hi(va0, vb0);
+      vl[2 * w + 1] = pair_lo(va1, vb1);
+      vh[2 * w + 1] = pair_hi(va1, vb1);
     }
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-      float s = 0.0f;
+      float sa0 = 0.0f, sa1 = 0.0f, sb0 = 0.0f, sb1 = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s = fmaf(qf[g][e], kf[e], s);
-      s = sum8(s);  // the row's 8 lanes, by DPP
-      if (valid) {
-        const float s2 = s * sc;
-        const float mn = fmaxf(m[g], s2);
-        const float corr = exp2_fast(m[g] - mn);
-        const float p = exp2_fast(s2 - mn);
-        l[g] = l[g] * corr + p;
+      for (int j = 0; j < 8; j += 2) {
+        sa0 = dot2_bf16(qp[g][j], ka[j], sa0);
+        sa1 = dot2_bf16(qp[g][j + 1], ka[j + 1], sa1);
+        sb0 = dot2_bf16(qp[g][j], kb[j], sb0);
+        sb1 = dot2_bf16(qp[g][j + 1], kb[j + 1], sb1);
+      }
+      const float sa = a_ok ? sum8(sa0 + sa1) * sc : -INFINITY;
+      const float sb = b_ok ? sum8(sb0 + sb1) * sc : -INFINITY;
+      // The reference max moves only when a score passes it by more than
+      // 2^8 (weights stay <= 256), so the rescale of l and acc is rare.
+      const float smax = fmaxf(sa, sb);
+      if (smax > m[g] + kF8Slack) {
+        const float corr = exp2_fast(m[g] - smax);
+        l[g] *= corr;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e] * corr);
-        m[g] = mn;
+        for (int e = 0; e < 16; ++e) acc[g][e] *= corr;
+        m[g] = smax;
+      }
+      const uint32_t pp = pack_bf16x2(exp2_fast(sa - m[g]), exp2_fast(sb - m[g]));
+      l[g] += bf16_lo(pp) + bf16_hi(pp);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[g][2 * j] = dot2_bf16(pp, vl[j], acc[g][2 * j]);
+        acc[g][2 * j + 1] = dot2_bf16(pp, vh[j], acc[g][2 * j + 1]);
       }
     }
   }
+  }  // blocks of the chunk
   // merge the 8 lane groups of the wave (lanes with the same dims differ in
   // bits 3..5): the bit-3 partner by a DPP row rotate, bits 4 and 5 by the
   // gfx950 permlane swaps (no LDS traffic). Both lanes of a pair form the same
@@ -228,7 +253,7 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_block_kernel(DecodeFp8A
   __syncthreads();
   // the block's partial for each head: threads 0..127 take one dim each
   if (tid < kF8D) {
-    const int64_t prow = (static_cast<int64_t>(seq) * a.max_blocks + b) * a.num_q_heads + hq0;
+    const int64_t prow = (static_cast<int64_t>(seq) * a.max_chunks + chunk) * a.num_q_heads + hq0;
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       float mm = kF8Empty;
@@ -257,10 +282,11 @@ __global__ __launch_bounds__(kF8D) void decode_fp8_merge_kernel(DecodeFp8Args a)
   const int d = threadIdx.x;
   const int ctx = min(max(a.context_lens[seq], 0), a.max_context_len);
   const int nb = (ctx + kTokensPerBlock - 1) / kTokensPerBlock;
-  if (nb == 0) return;  // empty context: the row stays unwritten
+  const int nc = (nb + a.blocks_per_chunk - 1) / a.blocks_per_chunk;
+  if (nc == 0) return;  // empty context: the row stays unwritten
   float mm = kF8Empty, ll = 0.0f, aa = 0.0f;
-  for (int b = 0; b < nb; ++b) {
-    const int64_t prow = (static_cast<int64_t>(seq) * a.max_blocks + b) * a.num_q_heads + hq;
+  for (int c = 0; c < nc; ++c) {
+    const int64_t prow = (static_cast<int64_t>(seq) * a.max_chunks + c) * a.num_q_heads + hq;
     const float mb = a.part_ml[2 * prow];
     const float lb = a.part_ml[2 * prow + 1];
     const float ab = a.part_acc[prow * kF8D + d];
@@ -293,7 +319,7 @@ hipError_t launch_kv_store_fp8(void* k_cache, void* v_cache, const void* k, cons
 hipError_t launch_decode_fp8(const DecodeFp8Args& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const int gt = decode_head_group(group);
-  const int64_t items = static_cast<int64_t>(a.num_seqs) * a.max_blocks * (a.num_q_heads / gt);
+  const int64_t items = static_cast<int64_t>(a.num_seqs) * a.max_chunks * (a.num_q_heads / gt);
   if (items == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>(items)), block(kF8Threads);
   if (gt == 4)

@@ -77,12 +77,24 @@ struct DecodeFp8Args {
   int32_t num_kv_heads;
   int32_t max_blocks_per_seq;
   int32_t max_context_len;
-  int32_t max_blocks;  // ceil(max_context_len / 256): block partials per sequence
+  int32_t blocks_per_chunk;  // 256-token blocks one workgroup streams (1, 2 or 4)
+  int32_t max_chunks;        // ceil(ceil(max_context_len / 256) / blocks_per_chunk): partials per sequence
   float scale_log2;    // scale * k_scale * log2(e)
   float v_scale;
-  float* part_ml;   // [num_seqs][max_blocks][num_q_heads][2]: running max (log2 units) and sum
-  float* part_acc;  // [num_seqs][max_blocks][num_q_heads][128]: unnormalised outputs
+  float* part_ml;   // [num_seqs][max_chunks][num_q_heads][2]: reference max (log2 units) and sum
+  float* part_acc;  // [num_seqs][max_chunks][num_q_heads][128]: unnormalised outputs
 };
+
+// Blocks one fp8 decode workgroup streams (its chunk of a sequence's
+// context): 4 while that still leaves at least kF8MinItems workgroups for the
+// largest contexts, else 2, else 1 -- long chunks save end-of-chunk merges,
+// short ones keep every CU busy.
+constexpr int64_t kF8MinItems = 4096;
+inline int32_t fp8_blocks_per_chunk(int64_t num_seqs, int64_t head_groups, int64_t max_blocks) {
+  for (int32_t bpc = 4; bpc > 1; bpc /= 2)
+    if (num_seqs * head_groups * ((max_blocks + bpc - 1) / bpc) >= kF8MinItems) return bpc;
+  return 1;
+}
 
 hipError_t launch_decode_fp8(const DecodeFp8Args& args, hipStream_t stream);
 
@@ -161,10 +173,11 @@ inline WorkspaceLayout make_workspace_layout(int64_t slot_rows, int64_t counters
   return w;
 }
 
-// Workspace of the fp8 decode: every (sequence, block, query head) partial.
-inline WorkspaceLayout decode_fp8_workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t max_blocks) {
+// Workspace of the fp8 decode: every (sequence, chunk, query head) partial
+// (sized by the caller for one-block chunks, the most partials).
+inline WorkspaceLayout decode_fp8_workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t max_chunks) {
   WorkspaceLayout w;
-  const int64_t rows = num_seqs * max_blocks * num_q_heads;
+  const int64_t rows = num_seqs * max_chunks * num_q_heads;
   w.lse_off = 0;
   w.out_off = static_cast<size_t>((rows * 2 * 4 + 255) / 256 * 256);
   w.counters_off = w.out_off + static_cast<size_t>(rows * 128 * 4);

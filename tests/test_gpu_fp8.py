@@ -96,3 +96,19 @@ def test_qwen3_0_6b_decode_workload_full_size():
     seqs = list(range(0, 64, 3))
     ref = f8.paged_attn_decode_fp8(c.q, kq, vq, c.block_tables, c.context_lens, c.scale, s, s, seqs=seqs)
     compare(out, ref, torch.bfloat16, rows=seqs)
+
+
+def test_decode_four_block_chunks():
+    """64 sequences, 32 Q / 8 KV heads, contexts up to 8192: enough work for
+    the decode to stream four blocks per workgroup (the other tests run one-
+    and two-block chunks)."""
+    say("fp8 decode four-block chunks")
+    rng = np.random.default_rng(77)
+    ctx = [int(x) for x in rng.integers(1, 8192, endpoint=True, size=64)]
+    ctx[0], ctx[1] = 8192, 1
+    scales = (0.0125, 0.0125)
+    c, kq, vq = fp8_case(77, ctx, 32, 8, scales)
+    out = run(c, kq, vq, scales)
+    seqs = [0, 1] + list(range(2, 64, 9))
+    ref = f8.paged_attn_decode_fp8(c.q, kq, vq, c.block_tables, c.context_lens, c.scale, *scales, seqs=seqs)
+    compare(out, ref, torch.bfloat16, rows=seqs)
