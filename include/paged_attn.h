@@ -192,10 +192,10 @@ pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache,
 
 /*
  * Number of workgroups pa_paged_attn_decode launches for these sizes on the
- * current device: two per compute unit when the kernel's occupancy allows it
- * (else as many as are resident at once), capped by the number of work units
- * and by 2048. 0 for sizes the library does not support. Queries the HIP
- * runtime (falls back to 256 compute units when no device is visible).
+ * current device: one per compute unit, capped by the number of work units,
+ * by 8 per (sequence, query-head group) item (small batches) and by 2048.
+ * 0 for sizes the library does not support. Queries the HIP runtime (falls
+ * back to 256 compute units when no device is visible).
  */
 int32_t pa_decode_num_workgroups(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len, pa_dtype dtype);

@@ -98,8 +98,9 @@ int32_t pa_decode_num_workgroups(int32_t num_seqs, int32_t num_q_heads, int32_t 
       num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128) || (dtype != PA_F32 && dtype != PA_BF16))
     return 0;
   const int32_t group = num_q_heads / num_kv_heads;
+  const int64_t items = static_cast<int64_t>(num_seqs) * (num_q_heads / pa::decode_head_group(group));
   return pa::decode_default_workgroups(dtype == PA_BF16 ? pa::Dtype::kBF16 : pa::Dtype::kF32, head_dim, group,
-                                       decode_max_units(num_seqs, num_q_heads, num_kv_heads, max_context_len));
+                                       decode_max_units(num_seqs, num_q_heads, num_kv_heads, max_context_len), items);
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_q_len,

@@ -99,8 +99,9 @@ inline int32_t fp8_blocks_per_chunk(int64_t num_seqs, int64_t head_groups, int64
 hipError_t launch_decode_fp8(const DecodeFp8Args& args, hipStream_t stream);
 
 
-// Grid the decode launcher uses when the caller does not fix one.
-int decode_default_workgroups(Dtype dtype, int32_t head_dim, int32_t group, int64_t max_units);
+// Grid the decode launcher uses when the caller does not fix one (`items` =
+// sequences x query-head groups).
+int decode_default_workgroups(Dtype dtype, int32_t head_dim, int32_t group, int64_t max_units, int64_t items);
 
 // Workgroups of `kernel` (with `threads` per workgroup) that are resident on
 // the current device at once: occupancy per compute unit (at most

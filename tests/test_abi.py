@@ -128,6 +128,9 @@ def test_decode_workspace_sizing():
     assert 1 <= n <= 64 * 8 * 16
     assert pa.decode_num_workgroups(1, 2, 1, 64, 1, torch.float32) == 1
     assert pa.decode_num_workgroups(1, 2, 1, 96, 100) == 0
+    # small batches: at most 8 workgroups per (sequence, query-head group) item
+    assert pa.decode_num_workgroups(1, 16, 8, 128, 4096) <= 8 * 8
+    assert pa.decode_num_workgroups(2, 32, 8, 128, 8192) <= 2 * 8 * 8
 
 
 def pre(**kw):
