@@ -245,3 +245,26 @@ def test_repeated_calls_one_workspace(workgroups):
             compare(out, ref, torch.bfloat16)
         else:
             assert torch.equal(bits(first), bits(out.cpu()))
+
+
+@pytest.mark.parametrize("workgroups", [0, 3, 64])
+def test_zero_length_contexts_are_skipped(workgroups):
+    """A context length of 0 (no token to attend to) leaves that output row
+    unwritten and does not disturb the others; the decode-step graphs rely on
+    it for their padding rows."""
+    say("decode zero-length contexts", workgroups)
+    c = ragged_case(15, [1, 700, 1, 300, 1], 8, 2, 128, torch.bfloat16)
+    ctx = c.context_lens.clone()
+    ctx[0] = 0
+    ctx[2] = 0
+    ctx[4] = 0
+    q = to_dev(c.q)
+    out = torch.full_like(q, 7.0)
+    pa.paged_attn_decode(out, q, to_dev(c.k_cache), to_dev(c.v_cache), to_dev(c.block_tables), to_dev(ctx),
+                         c.scale, c.max_context_len, num_workgroups=workgroups)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    for i in (0, 2, 4):
+        assert torch.all(got[i] == 7.0)
+    ref = oracle.paged_attn_decode(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.scale, seqs=[1, 3])
+    compare(got, ref, torch.bfloat16, rows=[1, 3])

@@ -94,3 +94,42 @@ def test_graph_replays_match_eager_and_oracle():
         ref = oracle.paged_attn_decode(q, kc_ref, vc_ref, bt, ctx, SCALE)
         compare(bufs["out"][:n], ref, torch.bfloat16)
     graphs.close()
+
+
+def test_non_power_of_two_max_batch():
+    """max_batch 12: buckets 1, 2, 4, 8, 12; a 10-sequence step runs the
+    12-bucket with two inert rows and matches the oracle."""
+    say("decode graphs: max batch 12")
+    rng = np.random.default_rng(31)
+    gen = torch.Generator().manual_seed(31)
+    maxb = 12
+    pool_k = torch.randn((NB, BS, HKV, D), generator=gen).to(torch.bfloat16)
+    pool_v = torch.randn((NB, BS, HKV, D), generator=gen).to(torch.bfloat16)
+    bufs = {
+        "out": torch.zeros((maxb, HQ, D), dtype=torch.bfloat16, device=DEV),
+        "q": torch.zeros((maxb, HQ, D), dtype=torch.bfloat16, device=DEV),
+        "k_new": torch.zeros((maxb, HKV, D), dtype=torch.bfloat16, device=DEV),
+        "v_new": torch.zeros((maxb, HKV, D), dtype=torch.bfloat16, device=DEV),
+        "slot_mapping": torch.full((maxb,), -1, dtype=torch.int32, device=DEV),
+        "block_tables": torch.full((maxb, MB), -1, dtype=torch.int32, device=DEV),
+        "context_lens": torch.zeros((maxb,), dtype=torch.int32, device=DEV),
+        "k_cache": pool_k.to(DEV),
+        "v_cache": pool_v.to(DEV),
+        "workspace": torch.zeros(pa.decode_workspace_bytes(maxb, HQ, D, MB * BS), dtype=torch.uint8, device=DEV),
+    }
+    graphs = DecodeGraphs(bufs, SCALE)
+    assert [graphs.bucket(n) for n in (1, 3, 8, 9, 12, 13)] == [1, 4, 8, 12, 12, 0]
+    n = 10
+    q, kn, vn, slots, bt, ctx = step_inputs(rng, gen, n)
+    for name, t in (("q", q), ("k_new", kn), ("v_new", vn), ("slot_mapping", slots), ("block_tables", bt),
+                    ("context_lens", ctx)):
+        bufs[name][:n].copy_(t.to(DEV))
+    graphs.launch(n)
+    torch.cuda.synchronize()
+    kc, vc = oracle.kv_store(pool_k, pool_v, kn, vn, slots)
+    assert torch.equal(bufs["k_cache"].cpu().view(torch.int16), kc.view(torch.int16))
+    ref = oracle.paged_attn_decode(q, kc, vc, bt, ctx, SCALE)
+    compare(bufs["out"][:n], ref, torch.bfloat16)
+    with pytest.raises(pa.PagedAttnError):
+        graphs.launch(13)
+    graphs.close()
