@@ -11,5 +11,5 @@ from .paged_attention import (  # noqa: F401
     paged_attn_decode,
     paged_attn_prefill,
 )
-from .rotary import rope, rope_angles, rope_kv_store  # noqa: F401
+from .rotary import qknorm_rope_kv_store, rms_norm, rope, rope_angles, rope_kv_store  # noqa: F401
 from .fp8_kv import dequantize as fp8_dequantize, kv_store_fp8, paged_attn_decode_fp8, quantize as fp8_quantize  # noqa: F401,E501

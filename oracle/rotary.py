@@ -59,6 +59,35 @@ def rope(x: torch.Tensor, positions: torch.Tensor, base: float) -> torch.Tensor:
     return torch.cat([a * cos - b * sin, b * cos + a * sin], dim=-1)
 
 
+def rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float) -> torch.Tensor:
+    """RMSNorm of every head row of x [T, H, D] over its D elements, float64:
+    x / sqrt(mean(x^2) + eps) * weight, weight [D] shared by all heads.
+
+    The pages name QK-Norm among the features of the served model ("Nano-vLLM
+    System Architecture Analysis", "Differences from Normal nanoGPT
+    Inference", item 6) without a formula; the reading taken is the RMS
+    normalisation of each query and key head row with a learned per-dimension
+    weight, applied before the rotary embedding.
+    """
+    x64 = x.to(torch.float64)
+    ms = (x64 * x64).mean(dim=-1, keepdim=True)
+    return x64 / torch.sqrt(ms + eps) * weight.to(torch.float64)
+
+
+def qknorm_rope_kv_store(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
+                         k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: torch.Tensor, base: float,
+                         q_weight: torch.Tensor, k_weight: torch.Tensor,
+                         eps: float) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """rope_kv_store with RMSNorm (QK-Norm) of q and k first: q and k head
+    rows are normalised (float64), rotated, and rounded once to the inputs'
+    dtype; v is stored as given."""
+    assert q.dtype == k.dtype == v.dtype
+    q_rot = rope(rms_norm(q, q_weight, eps), positions, base).to(q.dtype)
+    k_rot = rope(rms_norm(k, k_weight, eps), positions, base).to(k.dtype)
+    kc, vc = kv_store(k_cache, v_cache, k_rot, v, slot_mapping)
+    return q_rot, kc, vc
+
+
 def rope_kv_store(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
                   k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: torch.Tensor,
                   base: float) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:

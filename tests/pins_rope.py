@@ -98,7 +98,53 @@ def pin_rope_kv_store_placement(r):
     assert torch.equal(kc2[~touched], kc[~touched]) and torch.equal(vc2[~touched], vc[~touched])
 
 
+def pin_norm_unit_mean_square(r):
+    """Weight 1 and eps 0: every normalised head row has mean square 1."""
+    x = _x((4, 3, 16), 11) * 5.0
+    out = r.rms_norm(x, torch.ones(16, dtype=torch.float64), 0.0)
+    assert torch.allclose((out * out).mean(dim=-1), torch.ones(4, 3, dtype=torch.float64), rtol=0, atol=1e-13)
+
+
+def pin_norm_scale_invariant(r):
+    """eps 0: scaling a row by c > 0 does not change its normalised value."""
+    x = _x((2, 2, 8), 12)
+    w = _x((8,), 13)
+    assert torch.allclose(r.rms_norm(3.7 * x, w, 0.0), r.rms_norm(x, w, 0.0), rtol=0, atol=1e-13)
+
+
+def pin_norm_matches_library(r):
+    """The library's RMSNorm (torch, float64) over the last dimension."""
+    x = _x((3, 4, 32), 14)
+    w = _x((32,), 15)
+    ref = torch.nn.functional.rms_norm(x, (32,), w, 1e-6)
+    assert torch.allclose(r.rms_norm(x, w, 1e-6), ref, rtol=0, atol=1e-13)
+
+
+def pin_qknorm_rope_worked_d4(r):
+    """D = 4, x = (1, 2, 3, 4), weight (1, 2, 1, 0.5), eps 0.5, base 10000,
+    p = 1, worked by hand: mean square 7.5, + eps = 8, so x / sqrt 8 * w =
+    (1, 4, 3, 2) / (2 sqrt 2); pairs (x0, x2) turn by 1 rad and (x1, x3) by
+    10000^(-1/2) = 0.01 rad."""
+    x = torch.tensor([[[1.0, 2.0, 3.0, 4.0]]], dtype=torch.float64)
+    w = torch.tensor([1.0, 2.0, 1.0, 0.5], dtype=torch.float64)
+    z = torch.zeros(1, 1, 4, dtype=torch.float64)
+    kc = torch.zeros(1, 256, 1, 4, dtype=torch.float64)
+    q_rot, kcache, _ = r.qknorm_rope_kv_store(x, x, z, torch.tensor([1], dtype=torch.int32), kc, kc.clone(),
+                                              torch.tensor([5], dtype=torch.int32), 10000.0, w, w, 0.5)
+    c = 2.0 * math.sqrt(2.0)
+    a, b = 1.0, 0.01
+    want = torch.tensor([(1 * math.cos(a) - 3 * math.sin(a)) / c, (4 * math.cos(b) - 2 * math.sin(b)) / c,
+                         (3 * math.cos(a) + 1 * math.sin(a)) / c, (2 * math.cos(b) + 4 * math.sin(b)) / c],
+                        dtype=torch.float64)
+    assert torch.allclose(q_rot[0, 0], want, rtol=0, atol=1e-14)
+    assert torch.allclose(kcache[0, 5, 0], want, rtol=0, atol=1e-14)
+
+
 PINS = [
+    pin_norm_unit_mean_square,
+    pin_norm_scale_invariant,
+    pin_norm_matches_library,
+    pin_qknorm_rope_worked_d4,
     pin_rope_position_zero_is_identity,
     pin_rope_keeps_pair_lengths,
     pin_rope_relative_positions,

@@ -21,6 +21,12 @@ MUTATIONS = {
     "v_rotated": ("kv_store(k_cache, v_cache, k_rot, v, slot_mapping)",
                   "kv_store(k_cache, v_cache, k_rot, rope(v, positions, base).to(v.dtype), slot_mapping)"),
     "k_stored_plain": ("kv_store(k_cache, v_cache, k_rot, v, slot_mapping)", "kv_store(k_cache, v_cache, k, v, slot_mapping)"),
+    "norm_eps_dropped": ("torch.sqrt(ms + eps)", "torch.sqrt(ms)"),
+    "norm_sum_not_mean": ("(x64 * x64).mean(dim=-1, keepdim=True)", "(x64 * x64).sum(dim=-1, keepdim=True)"),
+    "norm_over_heads": ("(x64 * x64).mean(dim=-1, keepdim=True)", "(x64 * x64).mean(dim=(-2, -1), keepdim=True)"),
+    "norm_weight_dropped": ("/ torch.sqrt(ms + eps) * weight.to(torch.float64)", "/ torch.sqrt(ms + eps)"),
+    "norm_after_rope": ("q_rot = rope(rms_norm(q, q_weight, eps), positions, base).to(q.dtype)",
+                        "q_rot = rms_norm(rope(q, positions, base).unsqueeze(0)[0], q_weight, eps).to(q.dtype)"),
 }
 
 
