@@ -272,14 +272,24 @@ def run_rope_store(torch, pa, w, steps):
     def rope(_i):
         pa.rope_kv_store(q_out, kc, vc, q, k, v, pos_d, sm, ROPE_THETA)
 
+    qw = torch.ones(q.shape[2], dtype=q.dtype, device=dev)
+    kw = torch.ones(q.shape[2], dtype=q.dtype, device=dev)
+
+    def qknorm_rope(_i):
+        pa.qknorm_rope_kv_store(q_out, kc, vc, q, k, v, qw, kw, 1e-6, pos_d, sm, ROPE_THETA)
+
     for i in range(3):
         rope(i)
+        qknorm_rope(i)
     ms = time_launches(torch, rope, steps)
+    ms_norm = time_launches(torch, qknorm_rope, steps)
     elt = q.element_size()
     stored = int((c.slot_mapping >= 0).sum())
     nbytes = (2 * q.numel() + k.numel() + v.numel()) * elt + 2 * stored * k[0].numel() * elt + 2 * 4 * q.shape[0]
     return {"avg_us": round(ms * 1e3, 2), "TBps": round(nbytes / (ms * 1e-3) / 1e12, 4),
             "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "qknorm_avg_us": round(ms_norm * 1e3, 2),
+            "qknorm_frac_hbm_peak": round(nbytes / (ms_norm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": nbytes, "tokens": int(q.shape[0]), "stored_tokens": stored,
             "rope_theta": ROPE_THETA}
 

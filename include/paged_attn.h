@@ -137,6 +137,25 @@ pa_status pa_rope_kv_store(void* q_out, void* k_cache, void* v_cache, const void
                            pa_dtype dtype, pa_stream_t stream);
 
 /*
+ * pa_qknorm_rope_kv_store -- pa_rope_kv_store with QK-Norm first: every q and
+ * k head row x (head_dim elements) becomes x / sqrt(mean(x^2) + eps) * w,
+ * with w = q_norm_weight for q heads and k_norm_weight for k heads ([head_dim]
+ * each, in `dtype`, 16-byte aligned, shared by all heads), and is then rotated
+ * as in pa_rope_kv_store; v is stored as given. The pages list QK-Norm among
+ * the served model's features next to RoPE ("Nano-vLLM System Architecture
+ * Analysis", "Differences from Normal nanoGPT Inference", item 6) without a
+ * formula; the normalisation above is the reading taken. Arithmetic is fp32,
+ * with one rounding to `dtype` at the end. eps must be finite and >= 0; null
+ * weights are PA_ERR_INVALID_ARG. Other arguments and errors as in
+ * pa_rope_kv_store.
+ */
+pa_status pa_qknorm_rope_kv_store(void* q_out, void* k_cache, void* v_cache, const void* q, const void* k,
+                                  const void* v, const void* q_norm_weight, const void* k_norm_weight, float eps,
+                                  const int32_t* positions, const int32_t* slot_mapping, int32_t num_tokens,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float rope_theta, pa_dtype dtype, pa_stream_t stream);
+
+/*
  * pa_paged_attn_decode -- one query token per sequence attending over its
  * whole paged context.
  *

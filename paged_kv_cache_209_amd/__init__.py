@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     paged_attn_decode_fp8,
     paged_attn_prefill,
     prefill_workspace_bytes,
+    qknorm_rope_kv_store,
     rope_kv_store,
     version,
 )

@@ -41,6 +41,8 @@ SIGNATURES = {
     "pa_kv_store": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_rope_kv_store": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                 _i32, _vp]),
+    "pa_qknorm_rope_kv_store": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                       _i32, _i32, _f32, _i32, _vp]),
     "pa_paged_attn_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                     _f32, _i32, _vp, _sz, _vp]),
     "pa_paged_attn_decode_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -241,6 +243,30 @@ def paged_attn_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Ten
                                               int(max_context_len), float(scale), float(k_scale), float(v_scale),
                                               ws_ptr, ws_bytes, _stream(q)), "pa_paged_attn_decode_fp8")
     return out
+
+
+def qknorm_rope_kv_store(q_out: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, q: torch.Tensor,
+                         k: torch.Tensor, v: torch.Tensor, q_norm_weight: torch.Tensor, k_norm_weight: torch.Tensor,
+                         eps: float, positions: torch.Tensor, slot_mapping: torch.Tensor, rope_theta: float) -> None:
+    """pa_qknorm_rope_kv_store: RMSNorm (weights [D]) of q and k head rows,
+    then rope_kv_store."""
+    for name, t in (("q_out", q_out), ("k_cache", k_cache), ("v_cache", v_cache), ("q", q), ("k", k), ("v", v),
+                    ("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        _dev_tensor(t, name, k_cache.dtype)
+    _dev_tensor(positions, "positions", torch.int32)
+    _dev_tensor(slot_mapping, "slot_mapping", torch.int32)
+    nb, bs, hkv, d = k_cache.shape
+    if q.dim() != 3 or q.shape[2] != d or q_out.shape != q.shape or k.shape != (q.shape[0], hkv, d) or v.shape != k.shape:
+        raise ValueError("qknorm_rope_kv_store: q/q_out [T, Hq, D], k/v [T, Hkv, D] expected")
+    if q_norm_weight.shape != (d,) or k_norm_weight.shape != (d,):
+        raise ValueError("qknorm_rope_kv_store: norm weights must be [D]")
+    if positions.shape != (q.shape[0],) or slot_mapping.shape != (q.shape[0],):
+        raise ValueError("qknorm_rope_kv_store: positions and slot_mapping must be [T]")
+    _check(library().pa_qknorm_rope_kv_store(_ptr(q_out), _ptr(k_cache), _ptr(v_cache), _ptr(q), _ptr(k), _ptr(v),
+                                             _ptr(q_norm_weight), _ptr(k_norm_weight), float(eps), _ptr(positions),
+                                             _ptr(slot_mapping), q.shape[0], q.shape[1], hkv, d, bs, nb,
+                                             float(rope_theta), _dtype_code(k_cache), _stream(k_cache)),
+           "pa_qknorm_rope_kv_store")
 
 
 def decode_num_workgroups(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_context_len: int,

@@ -109,10 +109,15 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   return decode_workspace(num_seqs, num_q_heads, head_dim, max_context_len);
 }
 
-pa_status pa_rope_kv_store(void* q_out, void* k_cache, void* v_cache, const void* q, const void* k, const void* v,
-                           const int32_t* positions, const int32_t* slot_mapping, int32_t num_tokens,
-                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                           int32_t num_blocks, float rope_theta, pa_dtype dtype, pa_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+pa_status rope_store_common(void* q_out, void* k_cache, void* v_cache, const void* q, const void* k, const void* v,
+                            const void* q_weight, const void* k_weight, float eps, const int32_t* positions,
+                            const int32_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            float rope_theta, pa_dtype dtype, pa_stream_t stream) {
   if (num_tokens < 0 || num_q_heads <= 0) return PA_ERR_INVALID_ARG;
   const pa_status st = check_common(num_kv_heads, head_dim, block_size, num_blocks, dtype);
   if (st != PA_OK) return st;
@@ -139,9 +144,38 @@ pa_status pa_rope_kv_store(void* q_out, void* k_cache, void* v_cache, const void
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.base = rope_theta;
+  a.q_weight = q_weight;
+  a.k_weight = k_weight;
+  a.eps = eps;
   (void)hipGetLastError();
   return to_status(pa::launch_rope_kv_store(a, dtype == PA_BF16 ? pa::Dtype::kBF16 : pa::Dtype::kF32, head_dim,
                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_rope_kv_store(void* q_out, void* k_cache, void* v_cache, const void* q, const void* k, const void* v,
+                           const int32_t* positions, const int32_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, float rope_theta, pa_dtype dtype, pa_stream_t stream) {
+  return rope_store_common(q_out, k_cache, v_cache, q, k, v, nullptr, nullptr, 0.0f, positions, slot_mapping,
+                           num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, rope_theta, dtype,
+                           stream);
+}
+
+pa_status pa_qknorm_rope_kv_store(void* q_out, void* k_cache, void* v_cache, const void* q, const void* k,
+                                  const void* v, const void* q_norm_weight, const void* k_norm_weight, float eps,
+                                  const int32_t* positions, const int32_t* slot_mapping, int32_t num_tokens,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float rope_theta, pa_dtype dtype, pa_stream_t stream) {
+  if (q_norm_weight == nullptr || k_norm_weight == nullptr) return PA_ERR_INVALID_ARG;
+  if (!aligned16(q_norm_weight) || !aligned16(k_norm_weight)) return PA_ERR_INVALID_ARG;
+  if (!isfinite(eps) || eps < 0.0f) return PA_ERR_INVALID_ARG;
+  return rope_store_common(q_out, k_cache, v_cache, q, k, v, q_norm_weight, k_norm_weight, eps, positions,
+                           slot_mapping, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                           rope_theta, dtype, stream);
 }
 
 pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -24,6 +24,9 @@ struct RopeStoreArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   float base;  // rope theta
+  const void* q_weight;  // QK-Norm weights [head_dim] (both null: no normalisation)
+  const void* k_weight;
+  float eps;
 };
 
 hipError_t launch_rope_kv_store(const RopeStoreArgs& args, Dtype dtype, int32_t head_dim, hipStream_t stream);

@@ -1,5 +1,7 @@
 // Rotary position embedding of the new tokens' q and k, fused with the KV
-// store. The pages name RoPE among the features of the model Nano-vLLM serves
+// store (optionally after QK-Norm: RMSNorm of every q and k head row with a
+// per-dimension weight; the pages name QK-Norm among the served model's
+// features in the same list as RoPE). The pages name RoPE among the features of the model Nano-vLLM serves
 // ("Nano-vLLM System Architecture Analysis", section "Differences from Normal
 // nanoGPT Inference", item 6) and store each step's computed K/V into the
 // paged cache via slot_mapping (section 2, "Attention with Paged Cache"), so
@@ -60,7 +62,7 @@ struct alignas(sizeof(T) * P) Pack {
   T e[P];
 };
 
-template <typename T, int D>
+template <typename T, int D, bool NORM>
 __global__ __launch_bounds__(kRopeWaves * kWave) void rope_kv_store_kernel(RopeStoreArgs a) {
   constexpr int P = D / 2 / kLanesPerHead;  // pairs per lane
   using V = Pack<T, P>;
@@ -95,31 +97,54 @@ __global__ __launch_bounds__(kRopeWaves * kWave) void rope_kv_store_kernel(RopeS
   T* v_cache = static_cast<T*>(a.v_cache);
 
   // Rotates the two P-element pieces of one head row and writes them to dst
-  // (src and dst may be the same row).
-  auto rotate = [&](const T* src, T* dst) {
+  // (src and dst may be the same row). With NORM the row is first divided by
+  // its root mean square (the 16 lanes of the head sum their squares by lane
+  // shuffles) and multiplied by the per-dimension weight w.
+  auto rotate = [&](const T* src, T* dst, const T* w) {
     const V lo = *reinterpret_cast<const V*>(src + j * P);
     const V hi = *reinterpret_cast<const V*>(src + D / 2 + j * P);
+    float x[P], y[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      x[e] = to_f32<T>(lo.e[e]);
+      y[e] = to_f32<T>(hi.e[e]);
+    }
+    if constexpr (NORM) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int e = 0; e < P; ++e) ss = fmaf(x[e], x[e], fmaf(y[e], y[e], ss));
+#pragma unroll
+      for (int off = 1; off < kLanesPerHead; off <<= 1) ss += __shfl_xor(ss, off, kWave);
+      const float inv = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
+      const V wlo = *reinterpret_cast<const V*>(w + j * P);
+      const V whi = *reinterpret_cast<const V*>(w + D / 2 + j * P);
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        x[e] = x[e] * inv * to_f32<T>(wlo.e[e]);
+        y[e] = y[e] * inv * to_f32<T>(whi.e[e]);
+      }
+    }
     V olo, ohi;
 #pragma unroll
     for (int e = 0; e < P; ++e) {
-      const float x = to_f32<T>(lo.e[e]);
-      const float y = to_f32<T>(hi.e[e]);
-      olo.e[e] = from_f32<T>(x * cs[e] - y * sn[e]);
-      ohi.e[e] = from_f32<T>(y * cs[e] + x * sn[e]);
+      olo.e[e] = from_f32<T>(x[e] * cs[e] - y[e] * sn[e]);
+      ohi.e[e] = from_f32<T>(y[e] * cs[e] + x[e] * sn[e]);
     }
     *reinterpret_cast<V*>(dst + j * P) = olo;
     *reinterpret_cast<V*>(dst + D / 2 + j * P) = ohi;
   };
+  const T* q_w = static_cast<const T*>(a.q_weight);
+  const T* k_w = static_cast<const T*>(a.k_weight);
 
   for (int h0 = 0; h0 < a.num_q_heads; h0 += kHeadsPerPass) {
     const int h = h0 + hs;
-    if (h < a.num_q_heads) rotate(q + qrow + h * D, q_out + qrow + h * D);
+    if (h < a.num_q_heads) rotate(q + qrow + h * D, q_out + qrow + h * D, q_w);
   }
   if (slot < 0) return;  // the token's K/V are not stored (its query still is rotated)
   for (int h0 = 0; h0 < a.num_kv_heads; h0 += kHeadsPerPass) {
     const int h = h0 + hs;
     if (h < a.num_kv_heads) {
-      rotate(k + krow + h * D, k_cache + prow + h * D);
+      rotate(k + krow + h * D, k_cache + prow + h * D, k_w);
       const V lo = *reinterpret_cast<const V*>(v + krow + h * D + j * P);
       const V hi = *reinterpret_cast<const V*>(v + krow + h * D + D / 2 + j * P);
       *reinterpret_cast<V*>(v_cache + prow + h * D + j * P) = lo;
@@ -131,7 +156,10 @@ __global__ __launch_bounds__(kRopeWaves * kWave) void rope_kv_store_kernel(RopeS
 template <typename T, int D>
 hipError_t launch_typed(const RopeStoreArgs& a, hipStream_t stream) {
   const int blocks = (a.num_tokens + kRopeWaves - 1) / kRopeWaves;
-  rope_kv_store_kernel<T, D><<<dim3(static_cast<uint32_t>(blocks)), dim3(kRopeWaves * kWave), 0, stream>>>(a);
+  if (a.q_weight != nullptr)
+    rope_kv_store_kernel<T, D, true><<<dim3(static_cast<uint32_t>(blocks)), dim3(kRopeWaves * kWave), 0, stream>>>(a);
+  else
+    rope_kv_store_kernel<T, D, false><<<dim3(static_cast<uint32_t>(blocks)), dim3(kRopeWaves * kWave), 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -223,3 +223,22 @@ def test_fp8_validation():
     need = pa.decode_fp8_workspace_bytes(2, 8, 128, 1000)
     assert need == pa.decode_fp8_workspace_bytes(2, 8, 128, 1024) > 0
     assert pa.decode_fp8_workspace_bytes(2, 8, 64, 1000) == 0
+
+
+def test_qknorm_rope_validation():
+    lib = pa.library()
+
+    def call(**kw):
+        a = dict(qo=P, kc=P, vc=P, q=P, k=P, v=P, qw=P, kw=P, eps=1e-6, pos=P, slots=P, T=4, hq=4, hkv=2, d=128,
+                 bs=256, nb=8, theta=1e6, dt=pa.PA_BF16)
+        a.update(kw)
+        return lib.pa_qknorm_rope_kv_store(a["qo"], a["kc"], a["vc"], a["q"], a["k"], a["v"], a["qw"], a["kw"],
+                                           a["eps"], a["pos"], a["slots"], a["T"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                           a["nb"], a["theta"], a["dt"], None)
+
+    assert call(qw=None) == INVALID and call(kw=None) == INVALID
+    assert call(qw=P + 8) == INVALID
+    assert call(eps=-1.0) == INVALID and call(eps=float("nan")) == INVALID
+    assert call(d=96) == UNSUP
+    assert call(theta=0.0) == INVALID
+    assert call(T=0, q=None) == pa.PA_OK

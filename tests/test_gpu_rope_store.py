@@ -116,3 +116,36 @@ def test_chunked_prefill_workload_full_size():
     cached = [int(L) - m for L, m in zip(c.context_lens.tolist(), n)]
     pos = torch.cat([torch.arange(cached[i], cached[i] + n[i], dtype=torch.int32) for i in range(len(n))])
     check(c.q, c.k, c.v, c.k_cache, c.v_cache, pos, c.slot_mapping, torch.bfloat16)
+
+
+QK_SHAPES = [(16, 8, 128), (12, 4, 64), (6, 1, 128)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", QK_SHAPES, ids=[f"hq{s[0]}_hkv{s[1]}_d{s[2]}" for s in QK_SHAPES])
+def test_qknorm_matches_oracle(shape, dtype):
+    """QK-Norm (RMSNorm of every q and k head row, per-dimension weights)
+    before the rotation, against the fp64 oracle."""
+    hq, hkv, d = shape
+    say("qknorm rope store", shape, dtype)
+    q, k, v, kc, vc, pos, slots = case(31 + hq, 37, hq, hkv, d, dtype)
+    g = torch.Generator().manual_seed(5)
+    qw = (1.0 + 0.2 * torch.randn(d, generator=g)).to(dtype)
+    kw = (1.0 + 0.2 * torch.randn(d, generator=g)).to(dtype)
+    q = (q.float() * 3.0).to(dtype)  # rows far from unit RMS
+    eps = 1e-6
+    ref_q64 = oracle.rope(oracle.rms_norm(q, qw, eps), pos, THETA)
+    ref_k64 = oracle.rope(oracle.rms_norm(k, kw, eps), pos, THETA)
+    dkc, dvc = to_dev(kc), to_dev(vc)
+    qo = torch.empty_like(to_dev(q))
+    pa.qknorm_rope_kv_store(qo, dkc, dvc, to_dev(q), to_dev(k), to_dev(v), to_dev(qw), to_dev(kw), eps, to_dev(pos),
+                            to_dev(slots), THETA)
+    torch.cuda.synchronize()
+    compare(qo, ref_q64, dtype)
+    hkv_, d_ = k.shape[1], k.shape[2]
+    flat_k = dkc.cpu().reshape(-1, hkv_, d_)
+    flat_v = dvc.cpu().reshape(-1, hkv_, d_)
+    rows = stored_rows(slots)
+    tok = torch.tensor([i for i, s in enumerate(slots.tolist()) if s >= 0], dtype=torch.long)
+    compare(flat_k[rows], ref_k64[tok], dtype)
+    assert torch.equal(bits(flat_v[rows]), bits(v[tok]))
