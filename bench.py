@@ -414,17 +414,12 @@ def run_decode_graphs(torch, pa, steps):
     return res
 
 
-def run_block_manager(w, num_seqs, lo, hi, seed, steps, with_oracle):
-    """Host time of one decode step's metadata from the native block manager
-    (append one token to every sequence, then prepare_decode), on num_seqs
-    sequences with contexts uniform in [lo, hi] and 256-token blocks, the
+def block_manager_workload(num_seqs, lo, hi, seed, steps):
+    """Prompts of num_seqs sequences with contexts uniform in [lo, hi], the
     odd-numbered ones longer than 1024 tokens opening with one shared
-    1024-token system prompt; the plain-Python oracle of the
-    same manager is timed on the same steps when with_oracle is set."""
+    1024-token system prompt; a pool of 256-token blocks 1.25x their need
+    (plus room for `steps` decode tokens) and the table width."""
     import numpy as np
-
-    import oracle.block_manager as obm
-    from paged_kv_cache_209_amd.block_manager import BlockManager
 
     rng = np.random.default_rng(seed)
     lens = rng.integers(lo, hi, endpoint=True, size=num_seqs)
@@ -436,46 +431,37 @@ def run_block_manager(w, num_seqs, lo, hi, seed, steps, with_oracle):
         prompts.append((system if share else []) + tail)
     nb = int(1.25 * sum(-(-len(p) // 256) for p in prompts)) + num_seqs * ((steps + 3) // 256 + 2)
     width = max(-(-len(p) // 256) for p in prompts) + (steps + 3) // 256 + 2
-    res = {}
-    impls = [("native", BlockManager(nb, 256))]
-    if with_oracle:
-        impls.append(("oracle", obm.OracleBlockManager(nb, 256)))
-    for name, m in impls:
-        for i, p in enumerate(prompts):
-            m.allocate(i, p)
-        ids = list(range(num_seqs))
-        if name == "native":
-            m.prepare_prefill(ids, width)
-        else:
-            m.prepare_prefill(ids, None, width, 1 << 30)
-        if name == "native":
-            import torch
+    return prompts, nb, width
 
-            id_t = torch.arange(num_seqs, dtype=torch.int64)
-            tok_t = torch.full((num_seqs,), 7, dtype=torch.int32)
-            bufs = {"positions": torch.empty(num_seqs, dtype=torch.int32),
-                    "slot_mapping": torch.empty(num_seqs, dtype=torch.int32),
-                    "context_lens": torch.empty(num_seqs, dtype=torch.int32),
-                    "block_tables": torch.empty((num_seqs, width), dtype=torch.int32)}
-            for _ in range(3):
-                m.append_tokens(id_t, tok_t)
-                m.prepare_decode(id_t, width, out=bufs)
-            t0 = time.perf_counter()
-            for _ in range(steps):
-                m.append_tokens(id_t, tok_t)
-                m.prepare_decode(id_t, width, out=bufs)
-        else:
-            toks = [7] * num_seqs
-            for _ in range(3):
-                m.append_tokens(ids, toks)
-                m.prepare_decode(ids, width)
-            t0 = time.perf_counter()
-            for _ in range(steps):
-                m.append_tokens(ids, toks)
-                m.prepare_decode(ids, width)
-        res[f"{name}_us_per_step"] = round((time.perf_counter() - t0) / steps * 1e6, 1)
-    res.update({"num_seqs": num_seqs, "context_range": [lo, hi], "steps": steps, "num_blocks": nb})
-    return res
+
+def run_block_manager(num_seqs, lo, hi, seed, steps):
+    """Host time of one decode step's metadata from the native block manager
+    (append one token to every sequence, then prepare_decode into preallocated
+    buffers) after the whole prompts are admitted and prefilled."""
+    import torch
+
+    from paged_kv_cache_209_amd.block_manager import BlockManager
+
+    prompts, nb, width = block_manager_workload(num_seqs, lo, hi, seed, steps)
+    m = BlockManager(nb, 256)
+    for i, p in enumerate(prompts):
+        m.allocate(i, p)
+    m.prepare_prefill(list(range(num_seqs)), width)
+    id_t = torch.arange(num_seqs, dtype=torch.int64)
+    tok_t = torch.full((num_seqs,), 7, dtype=torch.int32)
+    bufs = {"positions": torch.empty(num_seqs, dtype=torch.int32),
+            "slot_mapping": torch.empty(num_seqs, dtype=torch.int32),
+            "context_lens": torch.empty(num_seqs, dtype=torch.int32),
+            "block_tables": torch.empty((num_seqs, width), dtype=torch.int32)}
+    for _ in range(3):
+        m.append_tokens(id_t, tok_t)
+        m.prepare_decode(id_t, width, out=bufs)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        m.append_tokens(id_t, tok_t)
+        m.prepare_decode(id_t, width, out=bufs)
+    return {"native_us_per_step": round((time.perf_counter() - t0) / steps * 1e6, 1), "num_seqs": num_seqs,
+            "context_range": [lo, hi], "steps": steps, "num_blocks": nb}
 
 
 def cpu_baseline(case, budget_s: float):
@@ -502,7 +488,30 @@ def cpu_baseline(case, budget_s: float):
     value = nbytes * frac / el / 1e12
     return {"value": value, "unit": "TB/s", "cores": torch.get_num_threads(), "kind": "oracle",
             "sample": f"{seqs_done} sequences of the config-2 decode step (store + decode, {frac:.2f} steps) "
-                      f"in {el:.1f} s on {cores} host cores, fp64"}
+                      f"in {el:.1f} s on {cores} host cores, fp64",
+            "block_manager_oracle_us_per_step": block_manager_oracle_step_us(64, 128, 4096, 1, 200)}
+
+
+def block_manager_oracle_step_us(num_seqs, lo, hi, seed, steps):
+    """The plain-Python oracle of the block manager on the same decode steps
+    as the native leg (append one token to every sequence, prepare_decode)."""
+    import oracle.block_manager as obm
+
+    prompts, nb, width = block_manager_workload(num_seqs, lo, hi, seed, steps)
+    m = obm.OracleBlockManager(nb, 256)
+    for i, p in enumerate(prompts):
+        m.allocate(i, p)
+    ids = list(range(num_seqs))
+    m.prepare_prefill(ids, None, width, 1 << 30)
+    toks = [7] * num_seqs
+    for _ in range(3):
+        m.append_tokens(ids, toks)
+        m.prepare_decode(ids, width)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        m.append_tokens(ids, toks)
+        m.prepare_decode(ids, width)
+    return round((time.perf_counter() - t0) / steps * 1e6, 1)
 
 
 def main():
@@ -659,8 +668,8 @@ def main():
         secondary["decode_step_graphs_vs_eager"] = run_decode_graphs(torch, pa, max(50, args.steps))
     if not args.skip_secondary and args.only in ("", "bm"):
         secondary["block_manager_decode_step_host"] = {
-            "c2_shape": run_block_manager(w, 64, 128, 4096, 1, 200, with_oracle=True),
-            "c4_shape": run_block_manager(w, 256, 1024, 8192, 3, 200, with_oracle=False),
+            "c2_shape": run_block_manager(64, 128, 4096, 1, 200),
+            "c4_shape": run_block_manager(256, 1024, 8192, 3, 200),
         }
     if secondary:
         result["secondary"] = secondary
