@@ -514,6 +514,21 @@ def block_manager_oracle_step_us(num_seqs, lo, hi, seed, steps):
     return round((time.perf_counter() - t0) / steps * 1e6, 1)
 
 
+def run_environment(torch, pa):
+    """Where the numbers were taken: GPU, compute units, host CPU and cores."""
+    props = torch.cuda.get_device_properties(0)
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"gpu": getattr(props, "gcnArchName", props.name), "compute_units": props.multi_processor_count,
+            "gpu_memory_gib": round(props.total_memory / 2**30, 1), "library": pa.version(),
+            "torch": torch.__version__, "hip": torch.version.hip, "cpu_model": cpu,
+            "host_cores_available": len(os.sched_getaffinity(0)), "host_cpu_count": os.cpu_count()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -673,6 +688,7 @@ def main():
         }
     if secondary:
         result["secondary"] = secondary
+    result["env"] = run_environment(torch, pa)
     if not args.skip_cpu and args.only in ("", "c2"):
         log("timing the fp64 oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline(w.config2(), args.cpu_seconds)
