@@ -210,6 +210,29 @@ pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache,
                                   size_t workspace_bytes, pa_stream_t stream);
 
 /*
+ * pa_paged_attn_decode_store -- the decode step in one launch: the store of
+ * the step's new K/V rows (pa_kv_store) fused with pa_paged_attn_decode.
+ *
+ * The pages store each step's computed K/V via slot_mapping and then attend
+ * over all cached K/V ("Nano-vLLM System Architecture Analysis", section 2,
+ * "Attention with Paged Cache"). Here sequence t's new token is k_new[t],
+ * v_new[t] ([num_seqs, num_kv_heads, head_dim], one new token per sequence,
+ * in sequence order): it is written to flat slot slot_mapping[t] of the pools
+ * (nothing when negative) and, within the same launch, read in flight as
+ * position context_lens[t] - 1 of the sequence's context. The result equals
+ * pa_kv_store followed by pa_paged_attn_decode whenever slot_mapping[t] is the
+ * slot of position context_lens[t] - 1 of sequence t (the engine's layout); no
+ * other sequence may read that slot in the same call. Other arguments, rules
+ * and errors as for pa_paged_attn_decode (library-chosen grid).
+ */
+pa_status pa_paged_attn_decode_store(void* out, const void* q, void* k_cache, void* v_cache, const void* k_new,
+                                     const void* v_new, const int32_t* slot_mapping, const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                     pa_dtype dtype, void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
  * Number of workgroups pa_paged_attn_decode launches for these sizes on the
  * current device: one per compute unit, capped by the number of work units,
  * by 8 per (sequence, query-head group) item (small batches) and by 2048.

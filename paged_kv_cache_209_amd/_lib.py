@@ -47,6 +47,8 @@ SIGNATURES = {
                                     _f32, _i32, _vp, _sz, _vp]),
     "pa_paged_attn_decode_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_paged_attn_decode_store": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                          _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_num_workgroups": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -300,6 +302,37 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
         nb, block_tables.shape[1], int(max_context_len), float(scale), _dtype_code(q), int(num_workgroups),
         _ptr(ws), ws_bytes, _stream(q))
     _check(status, "pa_paged_attn_decode")
+    return out
+
+
+def paged_attn_decode_store(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, max_context_len: int,
+                            workspace_tensor: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """pa_paged_attn_decode_store: store k_new/v_new [B, Hkv, D] at
+    slot_mapping and decode over the contexts in one launch (the new token of
+    sequence t is read in flight as its last position)."""
+    for name, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new),
+                    ("v_new", v_new)):
+        _dev_tensor(t, name, q.dtype)
+    _dev_tensor(slot_mapping, "slot_mapping", torch.int32)
+    _dev_tensor(block_tables, "block_tables", torch.int32)
+    _dev_tensor(context_lens, "context_lens", torch.int32)
+    nb, bs, hkv, d = k_cache.shape
+    b, hq, dq = q.shape
+    if out.shape != q.shape or dq != d or v_cache.shape != k_cache.shape or k_new.shape != (b, hkv, d) \
+            or v_new.shape != k_new.shape or slot_mapping.shape != (b,) or block_tables.dim() != 2 \
+            or block_tables.shape[0] != b or context_lens.shape != (b,):
+        raise ValueError("paged_attn_decode_store: shapes do not match")
+    need = decode_workspace_bytes(b, hq, d, max_context_len)
+    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need)
+    ws_ptr = None if ws is None else ws.data_ptr()
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(library().pa_paged_attn_decode_store(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new),
+                                                _ptr(v_new), _ptr(slot_mapping), _ptr(block_tables),
+                                                _ptr(context_lens), b, hq, hkv, d, bs, nb, block_tables.shape[1],
+                                                int(max_context_len), float(scale), _dtype_code(q), ws_ptr, ws_bytes,
+                                                _stream(q)), "pa_paged_attn_decode_store")
     return out
 
 

@@ -178,13 +178,19 @@ pa_status pa_qknorm_rope_kv_store(void* q_out, void* k_cache, void* v_cache, con
                            rope_theta, dtype, stream);
 }
 
-pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
-                                           const int32_t* block_tables, const int32_t* context_lens,
-                                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
-                                           pa_dtype dtype, int32_t num_workgroups, void* workspace,
-                                           size_t workspace_bytes, pa_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode, optionally fused with the store of the step's new K/V rows
+// (k_new non-null: k_new, v_new [num_seqs, num_kv_heads, head_dim] and
+// slot_mapping [num_seqs]).
+pa_status decode_common(void* out, const void* q, const void* k_cache, const void* v_cache, const void* k_new,
+                        const void* v_new, const int32_t* slot_mapping, const int32_t* block_tables,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                        int32_t max_context_len, float scale, pa_dtype dtype, int32_t num_workgroups,
+                        void* workspace, size_t workspace_bytes, pa_stream_t stream) {
   if (num_seqs < 0 || num_q_heads <= 0) return PA_ERR_INVALID_ARG;
   const pa_status st = check_common(num_kv_heads, head_dim, block_size, num_blocks, dtype);
   if (st != PA_OK) return st;
@@ -227,9 +233,40 @@ pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache,
   a.counters = split ? reinterpret_cast<int32_t*>(ws + lay.counters_off) : nullptr;
   a.part_lse = split ? reinterpret_cast<float*>(ws + lay.lse_off) : nullptr;
   a.part_out = split ? reinterpret_cast<float*>(ws + lay.out_off) : nullptr;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
   (void)hipGetLastError();
   return to_status(pa::launch_decode(a, dtype == PA_BF16 ? pa::Dtype::kBF16 : pa::Dtype::kF32, head_dim,
                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_paged_attn_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  float scale, pa_dtype dtype, int32_t num_workgroups, void* workspace,
+                                  size_t workspace_bytes, pa_stream_t stream) {
+  return decode_common(out, q, k_cache, v_cache, nullptr, nullptr, nullptr, block_tables, context_lens, num_seqs,
+                       num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       max_context_len, scale, dtype, num_workgroups, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_paged_attn_decode_store(void* out, const void* q, void* k_cache, void* v_cache, const void* k_new,
+                                     const void* v_new, const int32_t* slot_mapping, const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                     pa_dtype dtype, void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  if (num_seqs > 0 && (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr)) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!aligned16(k_new) || !aligned16(v_new))) return PA_ERR_INVALID_ARG;
+  return decode_common(out, q, k_cache, v_cache, num_seqs > 0 ? k_new : nullptr, v_new, slot_mapping, block_tables,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, max_context_len, scale, dtype, 0, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -147,23 +147,40 @@ struct Chunk {
   uint32_t ka[W], kb[W], va[W], vb[W];
 };
 
-template <typename T, int D>
+template <typename T, int D, bool FUSED>
 __device__ __forceinline__ void load_chunk(Chunk<DecodeShape<T, D>::kWords>& c, const T* kpool, const T* vpool,
-                                           int block, int64_t row_stride, int c0, int t_end, int ts, int sl) {
+                                           int block, int64_t row_stride, int c0, int t_end, int ts, int sl,
+                                           const T* knew, const T* vnew, int new_pos) {
   // Wave-uniform base of the chunk's first row plus a small per-lane offset.
   // Rows past the range are never read: their lanes re-read the last valid
   // row (always in the same block as the chunk start) and get zero weight.
+  // With FUSED, the row at position new_pos (the step's new token) comes from
+  // the call's in-flight knew/vnew rows instead of the pool.
   const int64_t r0 = static_cast<int64_t>(block) * kTokensPerBlock + (c0 % kTokensPerBlock);
   const T* kb = kpool + r0 * row_stride;
   const T* vb = vpool + r0 * row_stride;
   const int last = t_end - 1 - c0;
   const int rs = static_cast<int>(row_stride);
-  const int oa = min(ts, last) * rs;
-  const int ob = min(ts + 8, last) * rs;
-  load_row<T, D>(kb + oa, sl, c.ka);
-  load_row<T, D>(kb + ob, sl, c.kb);
-  load_row<T, D>(vb + oa, sl, c.va);
-  load_row<T, D>(vb + ob, sl, c.vb);
+  const int ra = min(ts, last), rb = min(ts + 8, last);
+  const T* ka = kb + ra * rs;
+  const T* va = vb + ra * rs;
+  const T* kbb = kb + rb * rs;
+  const T* vbb = vb + rb * rs;
+  if constexpr (FUSED) {
+    const int nr = new_pos - c0;
+    if (ra == nr) {
+      ka = knew;
+      va = vnew;
+    }
+    if (rb == nr) {
+      kbb = knew;
+      vbb = vnew;
+    }
+  }
+  load_row<T, D>(ka, sl, c.ka);
+  load_row<T, D>(kbb, sl, c.kb);
+  load_row<T, D>(va, sl, c.va);
+  load_row<T, D>(vbb, sl, c.vb);
 }
 
 // Block ids of a segment, one per lane, 64 at a time. Each chunk takes its id
@@ -303,6 +320,7 @@ struct Segment {
   int seq, hg;
   int t_lo, t_hi;        // tokens [t_lo, t_hi)
   int b_lo, b_hi;        // blocks [b_lo, b_hi) holding them
+  int last_pos;          // position of the sequence's last token (the step's new one)
   int n_parts;           // pieces of the item over all workgroups
   int64_t first_owner;   // workgroup holding the item's first piece
   int64_t item_first;    // the item's first cost unit (a virtual one)
@@ -350,6 +368,7 @@ struct SegmentWalk {
         s.hg = hg;
         s.t_lo = static_cast<int>(lo - real_first) * kDecodeUnitTokens;
         s.t_hi = min(min(ctx, max_ctx), static_cast<int>(seg_end - real_first) * kDecodeUnitTokens);
+        s.last_pos = min(ctx, max_ctx) - 1;
         s.b_lo = s.t_lo / kTokensPerBlock;
         s.b_hi = (s.t_hi + kTokensPerBlock - 1) / kTokensPerBlock;
         // lo < seg_end <= u_end: the item's real units start before the
@@ -448,7 +467,7 @@ __device__ __forceinline__ void merge_item(const DecodeArgs& a, T* out, int64_t 
     for (int k = 0; k < DL; ++k) store_out<T>(out + (unit0 + g) * D + k * kWave + lane, num[g][k] / den[g]);
 }
 
-template <typename T, int D, int GT>
+template <typename T, int D, int GT, bool FUSED>
 __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeArgs a) {
   using S = DecodeShape<T, D>;
   constexpr int W = S::kWords;
@@ -475,6 +494,25 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
   const int HG = a.num_q_heads / GT;  // head groups per sequence
   const int group = a.num_q_heads / a.num_kv_heads;
   const int groups_per_kv = group / GT;
+
+  // ---- 0. (FUSED) Store the step's new K/V rows, one token per sequence,
+  // token t by workgroup t mod grid. Nothing in this launch reads those pool
+  // rows: each sequence's new position is read from the in-flight rows.
+  if constexpr (FUSED) {
+    const int pieces = a.num_kv_heads * D * Elem<T>::kBytes / 16;  // 16-byte pieces per token row
+    for (int t = blockIdx.x; t < B; t += gridDim.x) {
+      const int slot = load_uniform(a.slot_mapping, t);
+      if (slot < 0) continue;
+      for (int p = tid; p < 2 * pieces; p += kDecodeThreads) {
+        const bool is_v = p >= pieces;
+        const int pp = is_v ? p - pieces : p;
+        const u32x4_t* src = static_cast<const u32x4_t*>(is_v ? a.v_new : a.k_new) + static_cast<int64_t>(t) * pieces;
+        u32x4_t* dst = static_cast<u32x4_t*>(const_cast<void*>(is_v ? a.v_cache : a.k_cache)) +
+                       static_cast<int64_t>(slot) * pieces;
+        dst[pp] = __builtin_nontemporal_load(src + pp);
+      }
+    }
+  }
 
   // ---- 1. Cost units: item (seq i, head group hg) costs one unit per 64
   // context tokens plus kItemCost units of fixed work, ordered seq-major.
@@ -554,6 +592,13 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
   const T* q = static_cast<const T*>(a.q);
   const T* k_cache = static_cast<const T*>(a.k_cache);
   const T* v_cache = static_cast<const T*>(a.v_cache);
+  // (FUSED) the in-flight K/V rows: token t = sequence t, [num_seqs, Hkv, D]
+  const T* knew_base = static_cast<const T*>(a.k_new);
+  const T* vnew_base = static_cast<const T*>(a.v_new);
+  const int nkv = a.num_kv_heads;
+  auto new_row = [nkv](const T* base, int seq, int kvh) -> const T* {
+    return FUSED ? base + (static_cast<int64_t>(seq) * nkv + kvh) * D : nullptr;
+  };
   LaneState<GT, E> st;
 
   // ---- 3. Stream the segments. While a segment streams, the next one's
@@ -592,8 +637,9 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
     t_end = real ? cs.t_hi : cs.t_lo;
     left = real ? (cs.t_hi - c + kStride - 1) / kStride : 1;
     const int kvh = cs.hg / groups_per_kv;
-    load_chunk<T, D>(cur, k_cache + kvh * D, v_cache + kvh * D, bw.get(c0 / kTokensPerBlock, lane), row_stride, c0,
-                     cs.t_hi, ts, sl);
+    load_chunk<T, D, FUSED>(cur, k_cache + kvh * D, v_cache + kvh * D, bw.get(c0 / kTokensPerBlock, lane), row_stride,
+                            c0, cs.t_hi, ts, sl, new_row(knew_base, cs.seq, kvh), new_row(vnew_base, cs.seq, kvh),
+                            cs.last_pos);
   }
 
   // Split-item pieces this workgroup stores (at most the first and the last
@@ -610,6 +656,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
     const int hq0 = kvh * group + (cs.hg % groups_per_kv) * GT;
     const T* kpool = k_cache + static_cast<int64_t>(kvh) * D;
     const T* vpool = v_cache + static_cast<int64_t>(kvh) * D;
+    const T* knew = new_row(knew_base, cs.seq, kvh);
+    const T* vnew = new_row(vnew_base, cs.seq, kvh);
 
     // The next segment (or, after the last one, this segment again, so that
     // the loads below are issued on every path): its block-table window and
@@ -643,11 +691,13 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
     int cn = c0;
     while (left > 2) {
       cn += kStride;
-      load_chunk<T, D>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi, ts, sl);
+      load_chunk<T, D, FUSED>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi, ts, sl,
+                              knew, vnew, cs.last_pos);
       consume_chunk<T, D, GT>(st, cur, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc);
       c0 += kStride;
       cn += kStride;
-      load_chunk<T, D>(cur, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi, ts, sl);
+      load_chunk<T, D, FUSED>(cur, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi, ts, sl,
+                              knew, vnew, cs.last_pos);
       consume_chunk<T, D, GT>(st, nxt, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc);
       c0 += kStride;
       left -= 2;
@@ -661,10 +711,13 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
     const T* n_vpool = v_cache + static_cast<int64_t>(n_kvh) * D;
     const bool two = left == 2;
     cn = two ? cn + kStride : cn;
-    load_chunk<T, D>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi, ts, sl);
+    load_chunk<T, D, FUSED>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi, ts, sl,
+                            knew, vnew, cs.last_pos);
     consume_chunk<T, D, GT>(st, cur, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc);
     c0 += kStride;
-    load_chunk<T, D>(cur, n_kpool, n_vpool, bwn.get(n_c0 / kTokensPerBlock, lane), row_stride, n_c0, ns.t_hi, ts, sl);
+    load_chunk<T, D, FUSED>(cur, n_kpool, n_vpool, bwn.get(n_c0 / kTokensPerBlock, lane), row_stride, n_c0, ns.t_hi,
+                            ts, sl, new_row(knew_base, ns.seq, n_kvh), new_row(vnew_base, ns.seq, n_kvh),
+                            ns.last_pos);
     consume_chunk<T, D, GT>(st, nxt, sq, sl, two && c0 + ts < t_end, two && c0 + 8 + ts < t_end, sc);
 
     // Merge the 8 lane groups of each wave into lanes 0-7: the upper half
@@ -795,30 +848,37 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
 constexpr int kDecodePerCu = 1;
 constexpr int64_t kDecodePiecesPerItem = 8;
 
-template <typename T, int D, int GT>
-hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+template <typename T, int D, int GT, bool FUSED>
+hipError_t launch_fused_or_not(const DecodeArgs& a, hipStream_t stream) {
   int wgs = a.num_workgroups;
   if (wgs <= 0) {
     const int64_t items = static_cast<int64_t>(a.num_seqs) * (a.num_q_heads / GT);
-    wgs = min(kDecodeMaxWorkgroups, resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, GT>),
-                                                        kDecodeThreads, a.max_units, kDecodePerCu));
+    wgs = min(kDecodeMaxWorkgroups,
+              resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, GT, FUSED>),
+                                  kDecodeThreads, a.max_units, kDecodePerCu));
     wgs = static_cast<int>(min(static_cast<int64_t>(wgs), max(int64_t{1}, items * kDecodePiecesPerItem)));
   }
-  paged_decode_kernel<T, D, GT><<<dim3(static_cast<uint32_t>(wgs)), dim3(kDecodeThreads), 0, stream>>>(a);
+  paged_decode_kernel<T, D, GT, FUSED><<<dim3(static_cast<uint32_t>(wgs)), dim3(kDecodeThreads), 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <typename T, int D, int GT>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  return a.k_new != nullptr ? launch_fused_or_not<T, D, GT, true>(a, stream)
+                            : launch_fused_or_not<T, D, GT, false>(a, stream);
 }
 
 template <typename T, int D>
 int default_grid(int group, int64_t max_units) {
   switch (decode_head_group(group)) {
     case 4:
-      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 4>), kDecodeThreads,
+      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 4, false>), kDecodeThreads,
                                  max_units, kDecodePerCu);
     case 2:
-      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 2>), kDecodeThreads,
+      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 2, false>), kDecodeThreads,
                                  max_units, kDecodePerCu);
     default:
-      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 1>), kDecodeThreads,
+      return resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, 1, false>), kDecodeThreads,
                                  max_units, kDecodePerCu);
   }
 }

@@ -49,6 +49,12 @@ struct DecodeArgs {
   int32_t* counters;  // [num_seqs * num_q_heads]: counted pieces of each split item; zero between calls
   float* part_lse;    // [2 * kDecodeMaxWorkgroups][group]: log2-sum-exp of each stored piece
   float* part_out;    // [2 * kDecodeMaxWorkgroups][group][head_dim]: normalised output of each piece
+  // Fused store (all null otherwise): sequence t's new token, [num_seqs,
+  // num_kv_heads, head_dim] each, is stored at slot_mapping[t] (if >= 0) and
+  // read in flight at position context_lens[t] - 1.
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slot_mapping;
 };
 
 // Decode work unit: 64 tokens of one (sequence, query-head group). Each item

@@ -1,0 +1,94 @@
+"""The decode step in one launch (pa_paged_attn_decode_store): the new
+tokens' K/V stored through slot_mapping and read in flight as each sequence's
+last position. Checked against the oracle's kv_store followed by decode
+(pools bit-exact, outputs within the fp32 / bf16 bars), bit for bit against
+the same step issued as two launches (pa_kv_store then pa_paged_attn_decode),
+with NaN in every pool row no context covers, and with a skipped slot (the
+token still attends in flight but is not stored)."""
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_209_amd as pa
+import workloads as w
+from gpu_util import DEV, bits, compare, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fused(c, kc, vc, slots=None):
+    q = to_dev(c.q)
+    out = torch.empty_like(q)
+    pa.paged_attn_decode_store(out, q, kc, vc, to_dev(c.k_new), to_dev(c.v_new),
+                               to_dev(c.slot_mapping if slots is None else slots), to_dev(c.block_tables),
+                               to_dev(c.context_lens), c.scale, c.max_context_len)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_two_launches(c, kc, vc):
+    q = to_dev(c.q)
+    out = torch.empty_like(q)
+    pa.kv_store(kc, vc, to_dev(c.k_new), to_dev(c.v_new), to_dev(c.slot_mapping))
+    pa.paged_attn_decode(out, q, kc, vc, to_dev(c.block_tables), to_dev(c.context_lens), c.scale, c.max_context_len)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_case(c, dtype, seqs=None):
+    kc_ref, vc_ref = oracle.kv_store(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping)
+    ref = oracle.paged_attn_decode(c.q, kc_ref, vc_ref, c.block_tables, c.context_lens, c.scale, seqs=seqs)
+    kc, vc = to_dev(c.k_cache), to_dev(c.v_cache)
+    out = run_fused(c, kc, vc)
+    assert torch.equal(bits(kc.cpu()), bits(kc_ref)) and torch.equal(bits(vc.cpu()), bits(vc_ref))
+    compare(out, ref, dtype, rows=seqs)
+    kc2, vc2 = to_dev(c.k_cache), to_dev(c.v_cache)
+    two = run_two_launches(c, kc2, vc2)
+    assert torch.equal(bits(out.cpu()), bits(two.cpu())), "fused and two-launch steps differ"
+    return out
+
+
+def test_tiny_fp32_decode_step():
+    """Four sequences, contexts 1, 37, 256, 513, fp32: the one-token context
+    returns its new V row bit for bit."""
+    say("fused step c1")
+    c = w.config1()
+    out = check_case(c, torch.float32).cpu()
+    for g in range(c.num_q_heads):
+        assert torch.equal(bits(out[0, g]), bits(c.v_new[0, g // (c.num_q_heads // c.num_kv_heads)]))
+
+
+def test_qwen3_0_6b_decode_step_full_size():
+    say("fused step c2")
+    check_case(w.config2(), torch.bfloat16)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (12, 4)], ids=["g1", "g2", "g4", "g3"])
+def test_ragged_poisoned(hq, hkv):
+    """Ragged contexts crossing block and 64-token unit edges, NaN in every
+    pool row that no context covers."""
+    say("fused step ragged", hq, hkv)
+    c = w.build_decode_case(f"fused{hq}", [1, 64, 65, 255, 256, 257, 1000, 3000], hq, hkv, 128, torch.bfloat16,
+                            40 + hq)
+    cov = w.covered_rows(c.block_tables, c.context_lens, c.num_blocks)
+    c.k_cache = w.poison_uncovered(c.k_cache, cov)
+    c.v_cache = w.poison_uncovered(c.v_cache, cov)
+    check_case(c, torch.bfloat16)
+
+
+def test_skipped_slot_attends_in_flight():
+    """slot -1: the token is not stored (its pool slot keeps its bytes) but it
+    is still position context_len - 1 of its sequence."""
+    say("fused step skipped slot")
+    c = w.build_decode_case("fused_skip", [5, 300, 40], 16, 8, 128, torch.bfloat16, 77)
+    kc_ref, vc_ref = oracle.kv_store(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping)
+    ref = oracle.paged_attn_decode(c.q, kc_ref, vc_ref, c.block_tables, c.context_lens, c.scale)
+    slots = c.slot_mapping.clone()
+    skipped = int(slots[1])
+    slots[1] = -1
+    kc, vc = to_dev(c.k_cache), to_dev(c.v_cache)
+    out = run_fused(c, kc, vc, slots)
+    compare(out, ref, torch.bfloat16)
+    hkv, d = c.k_cache.shape[2], c.k_cache.shape[3]
+    flat = kc.cpu().reshape(-1, hkv, d)
+    assert torch.equal(bits(flat[skipped]), bits(c.k_cache.reshape(-1, hkv, d)[skipped]))
