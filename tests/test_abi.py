@@ -242,3 +242,24 @@ def test_qknorm_rope_validation():
     assert call(d=96) == UNSUP
     assert call(theta=0.0) == INVALID
     assert call(T=0, q=None) == pa.PA_OK
+
+
+def fused(**kw):
+    a = dict(out=P, q=P, kc=P, vc=P, kn=P, vn=P, sl=P, bt=P, cl=P, B=4, hq=8, hkv=2, d=128, bs=256, nb=64, mb=16,
+             mc=4096, scale=0.088, dt=pa.PA_BF16, ws=None, wsb=0)
+    a.update(kw)
+    return pa.library().pa_paged_attn_decode_store(
+        a["out"], a["q"], a["kc"], a["vc"], a["kn"], a["vn"], a["sl"], a["bt"], a["cl"], a["B"], a["hq"], a["hkv"],
+        a["d"], a["bs"], a["nb"], a["mb"], a["mc"], a["scale"], a["dt"], a["ws"], a["wsb"], None)
+
+
+def test_decode_store_validation():
+    """The one-launch decode step rejects what pa_paged_attn_decode rejects,
+    plus missing or misaligned new-token rows and slot_mapping; an empty batch
+    is a no-op."""
+    for kw in (dict(kn=None), dict(vn=None), dict(sl=None), dict(kn=P + 8), dict(vn=P + 2), dict(q=None),
+               dict(bt=None), dict(hq=6, hkv=4), dict(mc=0), dict(scale=float("nan")), dict(dt=3)):
+        assert fused(**kw) == INVALID, kw
+    assert fused(d=80) == UNSUP
+    assert fused(ws=None, wsb=0) == WS
+    assert fused(B=0, out=None, q=None, kn=None, vn=None, sl=None, bt=None, cl=None) == pa.PA_OK
