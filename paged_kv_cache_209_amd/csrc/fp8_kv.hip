@@ -6,15 +6,17 @@
 // stored as the code nearest to clamp(x * (1/s), -448, 448) (ties to even, the
 // hardware converter's rounding) and read back as code * s.
 //
-// Decode works per (sequence, chunk of 1, 2 or 4 256-token blocks, group of GT
-// query heads of one KV head): one workgroup streams the chunk's K and V rows (128
-// bytes per row and head at D = 128) block by block and leaves an
-// online-softmax partial (reference max, sum, unnormalised output) in the
-// workspace; a second kernel merges a sequence's chunk partials in order
-// (deterministic, no atomics) and writes the bf16 output. Inside a workgroup
-// each wave takes 64 rows of each block: 8 lane groups of 8 lanes, a lane
-// holding 16 consecutive dims of a row, with all 8 of its rows' K and V loads
-// of a block issued before any arithmetic on them. q.k sums over the
+// Decode works per (sequence, chunk of 256-token blocks -- 1, 2, 4, or a
+// whole context of up to 32 -- group of GT query heads of one KV head): one
+// workgroup streams the chunk's K and V rows (128 bytes per row and head at
+// D = 128) block by block and leaves an online-softmax partial (reference
+// max, sum, unnormalised output) in the workspace; a second kernel merges a
+// sequence's chunk partials in order (deterministic, no atomics) and writes
+// the bf16 output. Inside a workgroup each wave takes 64 rows of each block:
+// 8 lane groups of 8 lanes, a lane holding 16 consecutive dims of a row. A
+// block's rows are loaded in two halves of 4 rows per lane; while one half is
+// consumed the other is in flight, and the consumed half's registers take the
+// same half of the next block. q.k sums over the
 // 8 lanes of a group by DPP; the 8 groups of a wave merge their softmax states
 // by a DPP row rotate and the gfx950 permlane swaps, the 4 waves through LDS.
 #include <math.h>
@@ -31,6 +33,7 @@ constexpr int kF8Waves = kF8Threads / kWave;
 constexpr int kF8D = 128;                       // head dim supported
 constexpr int kF8RowsPerWave = kTokensPerBlock / kF8Waves;  // 64
 constexpr int kF8Iters = kF8RowsPerWave / 8;    // rows per lane group
+constexpr int kF8Half = kF8Iters / 2;          // rows per lane group in one load half
 constexpr float kF8Empty = -1.0e30f;            // running max before any row
 constexpr float kF8Slack = 8.0f;                // log2 units the reference max may lag by
 
@@ -130,77 +133,120 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_block_kernel(DecodeFp8A
     for (int e = 0; e < 16; ++e) acc[g][e] = 0.0f;
   }
   const float sc = a.scale_log2;
+  // The block's rows are loaded in two halves (rows it * 8 + grp of the
+  // wave's 64 for it < 4, then it >= 4). While one half is consumed, the other
+  // is in flight; each consumed half's registers take the same half of the
+  // next block, so loads stay in flight across the whole chunk without extra
+  // registers. After the chunk's last block the refills read the current
+  // block's first row again (a cached line that is never used), which keeps
+  // the loop free of branches around loads.
+  const int64_t table_row = static_cast<int64_t>(seq) * a.max_blocks_per_seq;
+  auto block_base = [&](const void* pool, int blk) {
+    return static_cast<const uint8_t*>(pool) + (static_cast<int64_t>(blk) * kTokensPerBlock) * row_stride +
+           kvh * kF8D + sl * 16;
+  };
+  auto load_half = [&](const uint8_t* kbase, const uint8_t* vbase, int nrows, int it0, bool real,
+                       u32x4_t (&kr)[kF8Half], u32x4_t (&vr)[kF8Half]) {
+#pragma unroll
+    for (int i = 0; i < kF8Half; ++i) {
+      // past the context: re-read a row; not real: the block's first row
+      const int r = real ? min(wave * kF8RowsPerWave + (it0 + i) * 8 + grp, nrows - 1) : 0;
+      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kbase + r * row_stride));
+      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vbase + r * row_stride));
+    }
+  };
+  auto consume = [&](const u32x4_t (&kr)[kF8Half], const u32x4_t (&vr)[kF8Half], int it0, int nrows) {
+    // Two rows (a, b) per step: codes become bf16 pairs (exact), q.k is 8
+    // v_dot2_f32_bf16 per row, and p.V pairs the two rows in one v_dot2 per dim
+    // (p rounded to bf16, the sum l taken from the same rounded p). m is a
+    // reference, not necessarily the running max: l and acc are relative to it,
+    // which every later merge respects.
+#pragma unroll
+    for (int i = 0; i < kF8Half; i += 2) {
+      const int it = it0 + i;
+      const int ra = wave * kF8RowsPerWave + it * 8 + grp;
+      const bool a_ok = ra < nrows, b_ok = ra + 8 < nrows;
+      uint32_t ka[8], kb[8], vl[8], vh[8];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        ka[2 * w] = fp8x2_to_bf16x2<false>(kr[i][w]);
+        ka[2 * w + 1] = fp8x2_to_bf16x2<true>(kr[i][w]);
+        kb[2 * w] = fp8x2_to_bf16x2<false>(kr[i + 1][w]);
+        kb[2 * w + 1] = fp8x2_to_bf16x2<true>(kr[i + 1][w]);
+        const uint32_t va0 = fp8x2_to_bf16x2<false>(vr[i][w]), va1 = fp8x2_to_bf16x2<true>(vr[i][w]);
+        const uint32_t vb0 = fp8x2_to_bf16x2<false>(vr[i + 1][w]), vb1 = fp8x2_to_bf16x2<true>(vr[i + 1][w]);
+        // (v_a[e], v_b[e]) for dims e = 4w .. 4w+3
+        vl[2 * w] = pair_lo(va0, vb0);
+        vh[2 * w] = pair_hi(va0, vb0);
+        vl[2 * w + 1] = pair_lo(va1, vb1);
+        vh[2 * w + 1] = pair_hi(va1, vb1);
+      }
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float sa0 = 0.0f, sa1 = 0.0f, sb0 = 0.0f, sb1 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          sa0 = dot2_bf16(qp[g][j], ka[j], sa0);
+          sa1 = dot2_bf16(qp[g][j + 1], ka[j + 1], sa1);
+          sb0 = dot2_bf16(qp[g][j], kb[j], sb0);
+          sb1 = dot2_bf16(qp[g][j + 1], kb[j + 1], sb1);
+        }
+        // rows past the context (finite re-reads) get -inf without a branch
+        const float sa = fmaf(sum8(sa0 + sa1), sc, a_ok ? 0.0f : -INFINITY);
+        const float sb = fmaf(sum8(sb0 + sb1), sc, b_ok ? 0.0f : -INFINITY);
+        // The reference max moves only when a score passes it by more than
+        // 2^8 (weights stay <= 256), so the rescale of l and acc is rare.
+        const float smax = fmaxf(sa, sb);
+        if (smax > m[g] + kF8Slack) {
+          const float corr = exp2_fast(m[g] - smax);
+          l[g] *= corr;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[g][e] *= corr;
+          m[g] = smax;
+        }
+        const uint32_t pp = pack_bf16x2(exp2_fast(sa - m[g]), exp2_fast(sb - m[g]));
+        l[g] += bf16_lo(pp) + bf16_hi(pp);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          acc[g][2 * j] = dot2_bf16(pp, vl[j], acc[g][2 * j]);
+          acc[g][2 * j + 1] = dot2_bf16(pp, vh[j], acc[g][2 * j + 1]);
+        }
+      }
+    }
+  };
+  // Both halves of the first block are issued behind the query loads; the
+  // query rows are then waited for (an empty asm that reads them), so that the
+  // loop is entered, like its back edge, with exactly the two halves in
+  // flight, the older one first (scheduling barriers keep that order).
+  u32x4_t kA[kF8Half], vA[kF8Half], kB[kF8Half], vB[kF8Half];
+  int nrows = min(kTokensPerBlock, ctx - b_begin * kTokensPerBlock);
+  {
+    const int blk = load_uniform(a.block_tables, table_row + b_begin);
+    load_half(block_base(a.k_cache, blk), block_base(a.v_cache, blk), nrows, 0, true, kA, vA);
+    __builtin_amdgcn_sched_barrier(0);
+    load_half(block_base(a.k_cache, blk), block_base(a.v_cache, blk), nrows, kF8Half, true, kB, vB);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(qp[g][j]));
+  }
   for (int b = b_begin; b < b_end; ++b) {
-  const int nrows = min(kTokensPerBlock, ctx - b * kTokensPerBlock);
-  const int blk = a.block_tables[static_cast<int64_t>(seq) * a.max_blocks_per_seq + b];
-  // all of this lane's K and V rows of the block first
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache) +
-                         (static_cast<int64_t>(blk) * kTokensPerBlock) * row_stride + kvh * kF8D + sl * 16;
-  const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache) +
-                         (static_cast<int64_t>(blk) * kTokensPerBlock) * row_stride + kvh * kF8D + sl * 16;
-  u32x4_t kr[kF8Iters], vr[kF8Iters];
-#pragma unroll
-  for (int it = 0; it < kF8Iters; ++it) {
-    const int r = min(wave * kF8RowsPerWave + it * 8 + grp, nrows - 1);  // past the context: re-read a row
-    kr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kbase + r * row_stride));
-    vr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vbase + r * row_stride));
+    const bool more = b + 1 < b_end;
+    const int blk_n = load_uniform(a.block_tables, table_row + (more ? b + 1 : b));
+    const int nrows_n = more ? min(kTokensPerBlock, ctx - (b + 1) * kTokensPerBlock) : nrows;
+    const uint8_t* kbn = block_base(a.k_cache, blk_n);
+    const uint8_t* vbn = block_base(a.v_cache, blk_n);
+    consume(kA, vA, 0, nrows);
+    __builtin_amdgcn_sched_barrier(0);
+    load_half(kbn, vbn, nrows_n, 0, more, kA, vA);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(kB, vB, kF8Half, nrows);
+    __builtin_amdgcn_sched_barrier(0);
+    load_half(kbn, vbn, nrows_n, kF8Half, more, kB, vB);
+    __builtin_amdgcn_sched_barrier(0);
+    nrows = nrows_n;
   }
-  // Two rows (a, b) per step: codes become bf16 pairs (exact), q.k is 8
-  // v_dot2_f32_bf16 per row, and p.V pairs the two rows in one v_dot2 per dim
-  // (p rounded to bf16, the sum l taken from the same rounded p). m is a
-  // reference, not necessarily the running max: l and acc are relative to it,
-  // which every later merge respects.
-#pragma unroll
-  for (int it = 0; it < kF8Iters; it += 2) {
-    const int ra = wave * kF8RowsPerWave + it * 8 + grp;
-    const bool a_ok = ra < nrows, b_ok = ra + 8 < nrows;
-    uint32_t ka[8], kb[8], vl[8], vh[8];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      ka[2 * w] = fp8x2_to_bf16x2<false>(kr[it][w]);
-      ka[2 * w + 1] = fp8x2_to_bf16x2<true>(kr[it][w]);
-      kb[2 * w] = fp8x2_to_bf16x2<false>(kr[it + 1][w]);
-      kb[2 * w + 1] = fp8x2_to_bf16x2<true>(kr[it + 1][w]);
-      const uint32_t va0 = fp8x2_to_bf16x2<false>(vr[it][w]), va1 = fp8x2_to_bf16x2<true>(vr[it][w]);
-      const uint32_t vb0 = fp8x2_to_bf16x2<false>(vr[it + 1][w]), vb1 = fp8x2_to_bf16x2<true>(vr[it + 1][w]);
-      // (v_a[e], v_b[e]) for dims e = 4w .. 4w+3
-      vl[2 * w] = pair_lo(va0, vb0);
-      vh[2 * w] = pair_hi(va0, vb0);
-      vl[2 * w + 1] = pair_lo(va1, vb1);
-      vh[2 * w + 1] = pair_hi(va1, vb1);
-    }
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      float sa0 = 0.0f, sa1 = 0.0f, sb0 = 0.0f, sb1 = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        sa0 = dot2_bf16(qp[g][j], ka[j], sa0);
-        sa1 = dot2_bf16(qp[g][j + 1], ka[j + 1], sa1);
-        sb0 = dot2_bf16(qp[g][j], kb[j], sb0);
-        sb1 = dot2_bf16(qp[g][j + 1], kb[j + 1], sb1);
-      }
-      const float sa = a_ok ? sum8(sa0 + sa1) * sc : -INFINITY;
-      const float sb = b_ok ? sum8(sb0 + sb1) * sc : -INFINITY;
-      // The reference max moves only when a score passes it by more than
-      // 2^8 (weights stay <= 256), so the rescale of l and acc is rare.
-      const float smax = fmaxf(sa, sb);
-      if (smax > m[g] + kF8Slack) {
-        const float corr = exp2_fast(m[g] - smax);
-        l[g] *= corr;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[g][e] *= corr;
-        m[g] = smax;
-      }
-      const uint32_t pp = pack_bf16x2(exp2_fast(sa - m[g]), exp2_fast(sb - m[g]));
-      l[g] += bf16_lo(pp) + bf16_hi(pp);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        acc[g][2 * j] = dot2_bf16(pp, vl[j], acc[g][2 * j]);
-        acc[g][2 * j + 1] = dot2_bf16(pp, vh[j], acc[g][2 * j + 1]);
-      }
-    }
-  }
-  }  // blocks of the chunk
   // merge the 8 lane groups of the wave (lanes with the same dims differ in
   // bits 3..5): the bit-3 partner by a DPP row rotate, bits 4 and 5 by the
   // gfx950 permlane swaps (no LDS traffic). Both lanes of a pair form the same

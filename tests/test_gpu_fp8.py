@@ -2,7 +2,8 @@
 quantising store bit for bit (including saturating and subnormal values and
 skipped slots), and decode attention over fp8 pools within the bf16 bar for
 GQA groups 1, 2 and 4, ragged contexts, NaN codes in every row no context
-covers, the Qwen3-0.6B-shaped decode workload at full size, and repeated runs
+covers, chunks of 1, 2 and 4 blocks and whole contexts (split past 32
+blocks), the Qwen3-0.6B-shaped decode workload at full size, and repeated runs
 bit-identical."""
 import numpy as np
 import pytest
@@ -98,17 +99,64 @@ def test_qwen3_0_6b_decode_workload_full_size():
     compare(out, ref, torch.bfloat16, rows=seqs)
 
 
-def test_decode_four_block_chunks():
-    """64 sequences, 32 Q / 8 KV heads, contexts up to 8192: enough work for
-    the decode to stream four blocks per workgroup (the other tests run one-
-    and two-block chunks)."""
-    say("fp8 decode four-block chunks")
-    rng = np.random.default_rng(77)
-    ctx = [int(x) for x in rng.integers(1, 8192, endpoint=True, size=64)]
-    ctx[0], ctx[1] = 8192, 1
+@pytest.mark.parametrize("max_ctx,blocks", [(9216, 4), (4352, 2)], ids=["4blk", "2blk"])
+def test_decode_multi_block_chunks(max_ctx, blocks):
+    """60 sequences, 32 Q / 8 KV heads (480 items, too few for whole
+    contexts): contexts up to 9216 make the decode stream four blocks per
+    workgroup, up to 4352 two (the smaller tests run one-block chunks)."""
+    say(f"fp8 decode {blocks}-block chunks")
+    rng = np.random.default_rng(77 + blocks)
+    ctx = [int(x) for x in rng.integers(1, max_ctx, endpoint=True, size=60)]
+    ctx[0], ctx[1] = max_ctx, 1
     scales = (0.0125, 0.0125)
-    c, kq, vq = fp8_case(77, ctx, 32, 8, scales)
+    c, kq, vq = fp8_case(77 + blocks, ctx, 32, 8, scales)
     out = run(c, kq, vq, scales)
-    seqs = [0, 1] + list(range(2, 64, 9))
+    seqs = [0, 1] + list(range(2, 60, 9))
     ref = f8.paged_attn_decode_fp8(c.q, kq, vq, c.block_tables, c.context_lens, c.scale, *scales, seqs=seqs)
+    compare(out, ref, torch.bfloat16, rows=seqs)
+
+
+def test_decode_whole_context_chunks():
+    """64 sequences x 8 query-head groups = 512 items: a workgroup takes a
+    whole context of up to 32 blocks, and the two longest contexts (47 and 33
+    blocks) are split into a 32-block chunk and a remainder."""
+    say("fp8 decode whole-context chunks")
+    rng = np.random.default_rng(78)
+    ctx = [int(x) for x in rng.integers(1, 2000, endpoint=True, size=64)]
+    ctx[0], ctx[1], ctx[2] = 12000, 8193, 8192
+    scales = (0.0125, 0.02)
+    c, kq, vq = fp8_case(78, ctx, 32, 8, scales)
+    out = run(c, kq, vq, scales)
+    seqs = [0, 1, 2] + list(range(3, 64, 10))
+    ref = f8.paged_attn_decode_fp8(c.q, kq, vq, c.block_tables, c.context_lens, c.scale, *scales, seqs=seqs)
+    compare(out, ref, torch.bfloat16, rows=seqs)
+    again = run(c, kq, vq, scales)
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+
+
+def test_qwen3_8b_shared_prefix_full_size_sampled():
+    """The Qwen3-8B-shaped workload with a shared prefix at full size (batch
+    256, 32 Q / 8 KV heads, contexts U[1024, 8192]; whole-context chunks, as
+    the benchmark runs it): its bf16 pools quantised with scale 1/80 by torch
+    on the device (input generation), the oracle checks a sample of
+    sequences, sharers and non-sharers, shortest and longest."""
+    say("fp8 decode c4 full size")
+    c = w.config4(device=DEV)
+    s = 1.0 / 80.0
+
+    def codes(x):
+        return (x.to(torch.float32) * 80.0).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+    kq, vq = codes(c.k_cache), codes(c.v_cache)
+    out = torch.empty_like(c.q)
+    pa.paged_attn_decode_fp8(out, c.q, kq, vq, to_dev(c.block_tables), to_dev(c.context_lens), c.scale, s, s,
+                             c.max_context_len)
+    torch.cuda.synchronize()
+    ctx = c.context_lens.tolist()
+    sharers = set(c.meta["shared_seqs"])
+    picks = {int(np.argmin(ctx)), int(np.argmax(ctx))}
+    picks |= set(sorted(sharers)[:3]) | set([i for i in range(256) if i not in sharers][:3])
+    seqs = sorted(picks)
+    ref = f8.paged_attn_decode_fp8(c.q.cpu(), kq.cpu(), vq.cpu(), c.block_tables.cpu(), c.context_lens.cpu(), c.scale,
+                                   s, s, seqs=seqs)
     compare(out, ref, torch.bfloat16, rows=seqs)
