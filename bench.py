@@ -353,8 +353,9 @@ def run_fp8_decode(torch, pa, case, steps, copies):
 
 def run_decode_graphs(torch, pa, steps):
     """Decode steps (store of the new tokens + paged decode) issued eagerly
-    (two binding calls per step, exact max context) and as one graph launch
-    per step (bucket graphs captured for the table's 4096-token bound), at
+    (two binding calls per step, exact max context), eagerly as one launch
+    (pa_paged_attn_decode_store) and as one graph launch per step (bucket
+    graphs of that one kernel, captured for the table's 4096-token bound), at
     batch sizes 1, 4, 16 and 64 of Qwen3-0.6B-shaped sequences (16 Q / 8 KV
     heads, D 128, bf16, contexts uniform in [128, 4096]). Per step: wall time
     of `steps` back-to-back steps (host issue included) and GPU time from one
@@ -402,11 +403,16 @@ def run_decode_graphs(torch, pa, steps):
             pa.paged_attn_decode(bufs["out"][:n], bufs["q"][:n], kc, vc, bufs["block_tables"][:n], ctx_n,
                                  d ** -0.5, maxc, workspace_tensor=eager_ws)
 
+        def eager_one(_i):
+            pa.paged_attn_decode_store(bufs["out"][:n], bufs["q"][:n], kc, vc, bufs["k_new"][:n], bufs["v_new"][:n],
+                                       sm, bufs["block_tables"][:n], ctx_n, d ** -0.5, maxc,
+                                       workspace_tensor=eager_ws)
+
         def graph(_i):
             graphs.launch(n)
 
         row = {}
-        for name, fn in (("eager", eager), ("graph", graph)):
+        for name, fn in (("eager", eager), ("eager_one_launch", eager_one), ("graph", graph)):
             for i in range(5):
                 fn(i)
             torch.cuda.synchronize()

@@ -334,10 +334,13 @@ pa_status pa_paged_attn_decode_fp8(void* out, const void* q, const void* k_cache
                                    void* workspace, size_t workspace_bytes, pa_stream_t stream);
 
 /*
- * Decode-step graphs -- the store of the step's new K/V followed by paged
- * decode, captured once as HIP graphs for batch buckets 1, 2, 4, ... up to
- * max_batch (<= 512; the last bucket is max_batch itself) and replayed with
- * one launch per step.
+ * Decode-step graphs -- the store of the step's new K/V and paged decode, as
+ * pa_paged_attn_decode_store runs them (one kernel), captured once as HIP
+ * graphs for batch buckets 1, 2, 4, ... up to max_batch (<= 512; the last
+ * bucket is max_batch itself) and replayed with one launch per step. As for
+ * pa_paged_attn_decode_store, slot_mapping[t] must be the slot of position
+ * context_lens[t] - 1 of sequence t (or -1); the result then equals
+ * pa_kv_store followed by pa_paged_attn_decode.
  *
  * Defined by "Nano-vLLM System Architecture Analysis", section 2 "CUDA
  * Graphs" (decode steps captured as graphs, eager mode beyond 512 sequences)

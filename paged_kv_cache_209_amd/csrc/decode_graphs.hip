@@ -1,7 +1,8 @@
-// Decode-step graphs: the step's KV store followed by paged decode, captured
-// once per batch bucket (1, 2, 4, ... max_batch) as HIP graphs and replayed
-// with one launch ("Nano-vLLM System Architecture Analysis", section 2 "CUDA
-// Graphs"; "Differences from Normal nanoGPT Inference", item 4). A step of n
+// Decode-step graphs: the step's KV store and paged decode (one kernel, as
+// pa_paged_attn_decode_store runs them), captured once per batch bucket (1,
+// 2, 4, ... max_batch) as HIP graphs and replayed with one launch ("Nano-vLLM
+// System Architecture Analysis", section 2 "CUDA Graphs"; "Differences from
+// Normal nanoGPT Inference", item 4). A step of n
 // sequences runs the smallest bucket that holds it; the rows between n and the
 // bucket are made inert first (slot -1 stores nothing, context 0 writes no
 // output), by a small kernel launched outside the graph on the caller's
@@ -99,14 +100,11 @@ pa_status pa_decode_graphs_create(const pa_decode_graph_buffers* bufs, int32_t m
       st = PA_ERR_HIP;
       break;
     }
-    pa_status s1 = pa_kv_store(bufs->k_cache, bufs->v_cache, bufs->k_new, bufs->v_new, bufs->slot_mapping, b,
-                               num_kv_heads, head_dim, block_size, num_blocks, dtype, cap);
-    pa_status s2 = s1 == PA_OK
-                       ? pa_paged_attn_decode(bufs->out, bufs->q, bufs->k_cache, bufs->v_cache, bufs->block_tables,
-                                              bufs->context_lens, b, num_q_heads, num_kv_heads, head_dim,
-                                              block_size, num_blocks, max_blocks_per_seq, max_ctx, scale, dtype,
-                                              bufs->workspace, bufs->workspace_bytes, cap)
-                       : s1;
+    // one kernel node: the store of the new rows fused with the decode
+    const pa_status s2 = pa_paged_attn_decode_store(
+        bufs->out, bufs->q, bufs->k_cache, bufs->v_cache, bufs->k_new, bufs->v_new, bufs->slot_mapping,
+        bufs->block_tables, bufs->context_lens, b, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+        max_blocks_per_seq, max_ctx, scale, dtype, bufs->workspace, bufs->workspace_bytes, cap);
     hipGraph_t graph = nullptr;
     const hipError_t e = hipStreamEndCapture(cap, &graph);  // always leave capture mode
     if (s2 != PA_OK || e != hipSuccess || graph == nullptr) {
