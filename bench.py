@@ -329,7 +329,7 @@ def run_fp8_decode(torch, pa, case, steps, copies):
     out = torch.empty_like(q)
     bt, cl = case.block_tables.to(dev), case.context_lens.to(dev)
     maxc = case.max_context_len
-    ws = torch.empty(pa.decode_fp8_workspace_bytes(case.num_seqs, case.num_q_heads, d, maxc), dtype=torch.uint8,
+    ws = torch.zeros(pa.decode_fp8_workspace_bytes(case.num_seqs, case.num_q_heads, d, maxc), dtype=torch.uint8,
                      device=dev)
 
     def decode(i):

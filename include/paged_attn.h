@@ -314,18 +314,21 @@ pa_status pa_kv_store_fp8(void* k_cache, void* v_cache, const void* k, const voi
                           int32_t head_dim, int32_t block_size, int32_t num_blocks, float k_scale,
                           float v_scale, pa_stream_t stream);
 
-/* Workspace bytes of pa_paged_attn_decode_fp8: one partial (max, sum and
- * head_dim fp32 values) per (sequence, 256-token block, query head). Needs no
- * clearing. 0 for unsupported sizes. */
+/* Workspace bytes of pa_paged_attn_decode_fp8: the same as
+ * pa_decode_workspace_bytes for these sizes, under the same rule (zero-filled
+ * before the first call; every call leaves its counters zero; one workspace
+ * per stream of calls). 0 when none is needed or the sizes are unsupported
+ * (head_dim other than 128). */
 size_t pa_decode_fp8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                      int32_t max_context_len);
 
 /* pa_paged_attn_decode over fp8 pools: q and out bf16 [num_seqs,
  * num_q_heads, 128]; attention over the dequantised K/V (score =
  * scale * q.(code_k * k_scale), output = sum p (code_v * v_scale) / sum p),
- * fp32 accumulation, bf16 output rounded to nearest-even. Two launches on
- * `stream`: per-block partials, then an in-order merge (results bit-identical
- * from run to run). Same argument rules as pa_paged_attn_decode. */
+ * fp32 accumulation, bf16 output rounded to nearest-even. One launch on
+ * `stream`, the work split and in-kernel merge of pa_paged_attn_decode
+ * (results bit-identical from run to run). Same argument rules as
+ * pa_paged_attn_decode. */
 pa_status pa_paged_attn_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
                                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -229,6 +229,7 @@ pa_status decode_common(void* out, const void* q, const void* k_cache, const voi
   a.num_workgroups = num_workgroups;  // 0: one resident round, chosen by the launcher
   a.max_units = decode_max_units(num_seqs, num_q_heads, num_kv_heads, max_context_len);
   a.scale_log2 = scale * kLog2e;
+  a.v_scale = 1.0f;
   char* ws = static_cast<char*>(workspace);
   a.counters = split ? reinterpret_cast<int32_t*>(ws + lay.counters_off) : nullptr;
   a.part_lse = split ? reinterpret_cast<float*>(ws + lay.lse_off) : nullptr;
@@ -299,8 +300,8 @@ pa_status pa_kv_store_fp8(void* k_cache, void* v_cache, const void* k, const voi
 
 size_t pa_decode_fp8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                      int32_t max_context_len) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim != 128 || max_context_len <= 0) return 0;
-  return pa::decode_fp8_workspace_layout(num_seqs, num_q_heads, ceil_div(max_context_len, kBlockSize)).total;
+  if (head_dim != 128) return 0;
+  return decode_workspace(num_seqs, num_q_heads, head_dim, max_context_len);
 }
 
 pa_status pa_paged_attn_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -323,15 +324,14 @@ pa_status pa_paged_attn_decode_fp8(void* out, const void* q, const void* k_cache
   if (num_seqs == 0) return PA_OK;
   if (out == nullptr || q == nullptr || block_tables == nullptr || context_lens == nullptr) return PA_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID_ARG;
-  // the workspace holds one-block chunks, the most partials any call uses
-  const int64_t max_blocks = ceil_div(max_context_len, kBlockSize);
-  const pa::WorkspaceLayout lay = pa::decode_fp8_workspace_layout(num_seqs, num_q_heads, max_blocks);
-  const int32_t bpc = pa::fp8_blocks_per_chunk(num_seqs, num_q_heads / pa::decode_head_group(num_q_heads / num_kv_heads),
-                                               max_blocks);
-  const int32_t max_chunks = static_cast<int32_t>(ceil_div(max_blocks, bpc));
-  if (workspace == nullptr || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
-  pa::DecodeFp8Args a;
+  // the decode kernel's work split and workspace rule (counters zero between calls)
+  const pa::WorkspaceLayout lay = pa::decode_workspace_layout(num_seqs, num_q_heads);
+  const bool split = max_context_len > pa::kDecodeUnitTokens;
+  if (split) {
+    if (workspace == nullptr || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
+  }
+  pa::DecodeArgs a;
   a.out = out;
   a.q = q;
   a.k_cache = k_cache;
@@ -343,15 +343,19 @@ pa_status pa_paged_attn_decode_fp8(void* out, const void* q, const void* k_cache
   a.num_kv_heads = num_kv_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
-  a.blocks_per_chunk = bpc;
-  a.max_chunks = max_chunks;
+  a.num_workgroups = 0;
+  a.max_units = decode_max_units(num_seqs, num_q_heads, num_kv_heads, max_context_len);
   a.scale_log2 = scale * k_scale * kLog2e;
   a.v_scale = v_scale;
   char* ws = static_cast<char*>(workspace);
-  a.part_ml = reinterpret_cast<float*>(ws + lay.lse_off);
-  a.part_acc = reinterpret_cast<float*>(ws + lay.out_off);
+  a.counters = split ? reinterpret_cast<int32_t*>(ws + lay.counters_off) : nullptr;
+  a.part_lse = split ? reinterpret_cast<float*>(ws + lay.lse_off) : nullptr;
+  a.part_out = split ? reinterpret_cast<float*>(ws + lay.out_off) : nullptr;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
+  a.slot_mapping = nullptr;
   (void)hipGetLastError();
-  return to_status(pa::launch_decode_fp8(a, static_cast<hipStream_t>(stream)));
+  return to_status(pa::launch_decode_fp8_pools(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_q_len,

@@ -2,7 +2,10 @@
 // rows its block table names ("Nano-vLLM System Architecture Analysis",
 // section 2, "Attention with Paged Cache": decode attends over all cached K/V
 // of the sequence's blocks). Unlike a gather-then-attend implementation, the
-// rows are streamed from the pool in place and never copied.
+// rows are streamed from the pool in place and never copied. The pool element
+// type is fp32, bf16 or fp8 (E4M3 codes, read with bf16 q and out; each
+// lane's codes become exact bf16 pairs at consume time, the K pool's scale is
+// in the softmax scale and the V pool's is applied to the output).
 //
 // Work split. An item is (sequence, group of GT query heads sharing one KV
 // head); it costs one unit per 64 tokens of its context plus a fixed cost for
@@ -62,6 +65,9 @@ struct DecodeShape {
   static constexpr int kWords = kVecs * 4;  // 32-bit words per lane per row
   static constexpr int kLaneElems = kVecs * kElemsPerVec;
   static constexpr int kVecStride = 128 / Elem<T>::kBytes;  // elements between a lane's pieces
+  // 32-bit words of the lane's query elements (q has the pool's element type,
+  // bf16 for fp8 pools)
+  static constexpr int kQWords = kLaneElems * Elem<typename IoElem<T>::type>::kBytes / 4;
   static_assert(kRowBytes % 128 == 0, "head row must be a multiple of 128 bytes");
 };
 
@@ -102,11 +108,18 @@ __device__ __forceinline__ void load_row(const T* row, int sl, uint32_t (&w)[Dec
 
 // Partial q.k over the lane's elements.
 template <typename T, int D>
-__device__ __forceinline__ float partial_dot(const uint32_t (&qw)[DecodeShape<T, D>::kWords],
+__device__ __forceinline__ float partial_dot(const uint32_t (&qw)[DecodeShape<T, D>::kQWords],
                                              const uint32_t (&kw)[DecodeShape<T, D>::kWords]) {
   using S = DecodeShape<T, D>;
   float s0 = 0.0f, s1 = 0.0f;
-  if constexpr (Elem<T>::kBytes == 2) {
+  if constexpr (Elem<T>::kBytes == 1) {
+    // fp8 codes, four per word, become bf16 pairs (exact) for the bf16 q
+#pragma unroll
+    for (int w = 0; w < S::kWords; ++w) {
+      s0 = dot2_bf16(qw[2 * w], fp8x2_to_bf16x2<false>(kw[w]), s0);
+      s1 = dot2_bf16(qw[2 * w + 1], fp8x2_to_bf16x2<true>(kw[w]), s1);
+    }
+  } else if constexpr (Elem<T>::kBytes == 2) {
 #pragma unroll
     for (int w = 0; w < S::kWords; w += 2) {
       s0 = dot2_bf16(qw[w], kw[w], s0);
@@ -216,8 +229,19 @@ struct BlockWindow {
 // The lane's words of query head g, read from the wave's copy of the group's
 // query rows in LDS (the same pieces of the row that the lane loads of K).
 template <typename T, int D>
-__device__ __forceinline__ void q_words(const u32x4_t* sq, int g, int sl, uint32_t (&w)[DecodeShape<T, D>::kWords]) {
+__device__ __forceinline__ void q_words(const u32x4_t* sq, int g, int sl, uint32_t (&w)[DecodeShape<T, D>::kQWords]) {
   using S = DecodeShape<T, D>;
+  if constexpr (Elem<T>::kBytes == 1) {
+    // fp8 pools: the lane's 16 consecutive dims of the bf16 query row
+    const u32x4_t x0 = sq[(g * D + sl * 16) / 8];
+    const u32x4_t x1 = sq[(g * D + sl * 16) / 8 + 1];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      w[k] = x0[k];
+      w[4 + k] = x1[k];
+    }
+    return;
+  }
 #pragma unroll
   for (int v = 0; v < S::kVecs; ++v) {
     const u32x4_t x = sq[(g * D + v * S::kVecStride + sl * S::kElemsPerVec) * Elem<T>::kBytes / 16];
@@ -238,7 +262,7 @@ __device__ __forceinline__ void consume_chunk(LaneState<GT, DecodeShape<T, D>::k
   bool need = false;
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
-    uint32_t qw[W];
+    uint32_t qw[DecodeShape<T, D>::kQWords];
     q_words<T, D>(sq, g, sl, qw);
     const float da = sum8(partial_dot<T, D>(qw, c.ka));
     const float db = sum8(partial_dot<T, D>(qw, c.kb));
@@ -257,12 +281,25 @@ __device__ __forceinline__ void consume_chunk(LaneState<GT, DecodeShape<T, D>::k
       st.m[g] = mn;
     }
   }
-  if constexpr (Elem<T>::kBytes == 2) {
+  if constexpr (Elem<T>::kBytes <= 2) {
     uint32_t vp[E];
+    if constexpr (Elem<T>::kBytes == 1) {
+      // fp8: word w holds elements 4w .. 4w+3 of each row
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-      vp[2 * w] = pair_lo(c.va[w], c.vb[w]);
-      vp[2 * w + 1] = pair_hi(c.va[w], c.vb[w]);
+      for (int w = 0; w < W; ++w) {
+        const uint32_t a0 = fp8x2_to_bf16x2<false>(c.va[w]), a1 = fp8x2_to_bf16x2<true>(c.va[w]);
+        const uint32_t b0 = fp8x2_to_bf16x2<false>(c.vb[w]), b1 = fp8x2_to_bf16x2<true>(c.vb[w]);
+        vp[4 * w] = pair_lo(a0, b0);
+        vp[4 * w + 1] = pair_hi(a0, b0);
+        vp[4 * w + 2] = pair_lo(a1, b1);
+        vp[4 * w + 3] = pair_hi(a1, b1);
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        vp[2 * w] = pair_lo(c.va[w], c.vb[w]);
+        vp[2 * w + 1] = pair_hi(c.va[w], c.vb[w]);
+      }
     }
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
@@ -414,7 +451,7 @@ __device__ __forceinline__ int64_t piece_slot(const EvenSplit& split, int64_t fi
   return p > 0 || split.start(w) >= item_first ? 2 * w : 2 * w + 1;
 }
 
-template <typename T, int D, int GT>
+template <typename T, int D, int GT, bool kOutScale>
 __device__ __forceinline__ void merge_item(const DecodeArgs& a, T* out, int64_t unit0, const EvenSplit& split,
                                            int64_t first_owner, int n_parts, int64_t item_first, int lane) {
   constexpr int DL = D / kWave;                             // dims per lane
@@ -464,16 +501,21 @@ __device__ __forceinline__ void merge_item(const DecodeArgs& a, T* out, int64_t 
 #pragma unroll
   for (int g = 0; g < GT; ++g)
 #pragma unroll
-    for (int k = 0; k < DL; ++k) store_out<T>(out + (unit0 + g) * D + k * kWave + lane, num[g][k] / den[g]);
+    for (int k = 0; k < DL; ++k) {
+      const float o = num[g][k] / den[g];
+      store_out<T>(out + (unit0 + g) * D + k * kWave + lane, kOutScale ? o * a.v_scale : o);
+    }
 }
 
 template <typename T, int D, int GT, bool FUSED>
 __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeArgs a) {
   using S = DecodeShape<T, D>;
+  using IoT = typename IoElem<T>::type;  // q and out (bf16 for fp8 pools)
+  constexpr bool kOutScale = Elem<T>::kBytes == 1;  // fp8 pools: out *= the V pool's scale
   constexpr int W = S::kWords;
   constexpr int E = S::kLaneElems;
   constexpr int kStride = kDecodeWaves * kChunk;  // tokens between a wave's chunks
-  constexpr int kQVecs = GT * D * Elem<T>::kBytes / 16;  // 16-byte pieces of a group's query rows
+  constexpr int kQVecs = GT * D * Elem<IoT>::kBytes / 16;  // 16-byte pieces of a group's query rows
   constexpr int kQPerLane = (kQVecs + kWave - 1) / kWave;
   __shared__ int s_wsum[kDecodeWaves];
   __shared__ int s_loc[3];
@@ -588,8 +630,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
 
   const int64_t row_stride = static_cast<int64_t>(a.num_kv_heads) * D;
   const float sc = a.scale_log2;
-  T* out = static_cast<T*>(a.out);
-  const T* q = static_cast<const T*>(a.q);
+  IoT* out = static_cast<IoT*>(a.out);
+  const IoT* q = static_cast<const IoT*>(a.q);
   const T* k_cache = static_cast<const T*>(a.k_cache);
   const T* v_cache = static_cast<const T*>(a.v_cache);
   // (FUSED) the in-flight K/V rows: token t = sequence t, [num_seqs, Hkv, D]
@@ -781,7 +823,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
       }
       const float val = num / den;
       if (cs.n_parts == 1) {
-        store_out<T>(out + (unit0 + g) * D + d, val);
+        store_out<IoT>(out + (unit0 + g) * D + d, kOutScale ? val * a.v_scale : val);
       } else {
         // A piece of a split item: its normalised output and log2-sum-exp go
         // to the piece's slot, written through to the device-coherent level
@@ -828,11 +870,13 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
     const int t0 = __builtin_amdgcn_readlane(t, 0);
     const int t1 = __builtin_amdgcn_readlane(t, 1);
     if (t0 == kDecodeWaves * pend_n[0] - 1) {
-      merge_item<T, D, GT>(a, out, pend_unit0[0], split, pend_first[0], pend_n[0], pend_item_first[0], lane);
+      merge_item<IoT, D, GT, kOutScale>(a, out, pend_unit0[0], split, pend_first[0], pend_n[0], pend_item_first[0],
+                                        lane);
       if (lane == 0) store_agent_int(a.counters + pend_item[0], 0);
     }
     if (pend_item[1] >= 0 && t1 == kDecodeWaves * pend_n[1] - 1) {
-      merge_item<T, D, GT>(a, out, pend_unit0[1], split, pend_first[1], pend_n[1], pend_item_first[1], lane);
+      merge_item<IoT, D, GT, kOutScale>(a, out, pend_unit0[1], split, pend_first[1], pend_n[1], pend_item_first[1],
+                                        lane);
       if (lane == 0) store_agent_int(a.counters + pend_item[1], 0);
     }
   }
@@ -846,6 +890,10 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
 // stores and merge latency than it gains (batch 1, Qwen3-0.6B shape: 26 us
 // at 256 workgroups, 13 us at 64).
 constexpr int kDecodePerCu = 1;
+// fp8 pools: a lane loads half the bytes of a bf16 row per token, so one
+// workgroup per CU keeps too few bytes in flight; two per CU measured 64 us
+// against 66-69 us (one) and 67 us (three) on the Qwen3-0.6B-shaped decode.
+constexpr int kDecodePerCuFp8 = 2;
 constexpr int64_t kDecodePiecesPerItem = 8;
 
 template <typename T, int D, int GT, bool FUSED>
@@ -855,7 +903,7 @@ hipError_t launch_fused_or_not(const DecodeArgs& a, hipStream_t stream) {
     const int64_t items = static_cast<int64_t>(a.num_seqs) * (a.num_q_heads / GT);
     wgs = min(kDecodeMaxWorkgroups,
               resident_workgroups(reinterpret_cast<const void*>(&paged_decode_kernel<T, D, GT, FUSED>),
-                                  kDecodeThreads, a.max_units, kDecodePerCu));
+                                  kDecodeThreads, a.max_units, Elem<T>::kBytes == 1 ? kDecodePerCuFp8 : kDecodePerCu));
     wgs = static_cast<int>(min(static_cast<int64_t>(wgs), max(int64_t{1}, items * kDecodePiecesPerItem)));
   }
   paged_decode_kernel<T, D, GT, FUSED><<<dim3(static_cast<uint32_t>(wgs)), dim3(kDecodeThreads), 0, stream>>>(a);
@@ -896,6 +944,17 @@ hipError_t launch_group(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_decode_fp8_pools(const DecodeArgs& a, hipStream_t stream) {
+  switch (decode_head_group(a.num_q_heads / a.num_kv_heads)) {
+    case 4:
+      return launch_fused_or_not<fp8_t, 128, 4, false>(a, stream);
+    case 2:
+      return launch_fused_or_not<fp8_t, 128, 2, false>(a, stream);
+    default:
+      return launch_fused_or_not<fp8_t, 128, 1, false>(a, stream);
+  }
+}
 
 hipError_t launch_decode(const DecodeArgs& a, Dtype dtype, int32_t head_dim, hipStream_t stream) {
   if (dtype == Dtype::kBF16) {

@@ -31,6 +31,27 @@ struct Elem<bf16_t> {
   static constexpr int kBytes = 2;
 };
 
+// fp8 KV-cache element: one OCP E4M3 code (the pool's scale is applied by
+// the kernels that read it).
+struct fp8_t {
+  uint8_t bits;
+};
+template <>
+struct Elem<fp8_t> {
+  static constexpr int kBytes = 1;
+};
+
+// Element type of the tensors a pool element type is read with (q, out and
+// the in-flight K/V rows): the pool's own, bf16 for fp8 pools.
+template <typename T>
+struct IoElem {
+  using type = T;
+};
+template <>
+struct IoElem<fp8_t> {
+  using type = bf16_t;
+};
+
 // bf16 <-> fp32. Widening is exact (the bf16 pattern is the top half of the
 // fp32 pattern); narrowing rounds to nearest-even through the hardware
 // converter (v_cvt_pk_bf16_f32).
@@ -40,6 +61,15 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two E4M3 codes (the low or the high 16 bits of w, the first code in the
+// lower byte) as a bf16 pair, the first code in the low half: gfx950's
+// scaled converter with scale 1, which is exact (every E4M3 value is a bf16
+// value).
+template <bool kHigh>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
 }
 
 __device__ __forceinline__ uint16_t to_bf16_bits(float x) {

@@ -45,7 +45,8 @@ struct DecodeArgs {
   int32_t max_context_len;
   int32_t num_workgroups;  // the context work is split evenly over this many (0: the library's grid)
   int64_t max_units;       // upper bound of the work units (the grid never exceeds it)
-  float scale_log2;   // scale * log2(e): scores are kept in base-2 units
+  float scale_log2;   // scale * log2(e) (times the K pool's scale for fp8 pools): scores in base-2 units
+  float v_scale;      // fp8 pools: the V pool's scale, applied to the output; 1 otherwise
   int32_t* counters;  // [num_seqs * num_q_heads]: counted pieces of each split item; zero between calls
   float* part_lse;    // [2 * kDecodeMaxWorkgroups][group]: log2-sum-exp of each stored piece
   float* part_out;    // [2 * kDecodeMaxWorkgroups][group][head_dim]: normalised output of each piece
@@ -69,53 +70,14 @@ constexpr int32_t kDecodeMaxGroup = 4;  // query heads per decode workgroup
 
 hipError_t launch_decode(const DecodeArgs& args, Dtype dtype, int32_t head_dim, hipStream_t stream);
 
-// fp8 (E4M3) KV cache: quantising store and decode.
+// fp8 (E4M3) KV cache: the quantising store.
 hipError_t launch_kv_store_fp8(void* k_cache, void* v_cache, const void* k, const void* v,
                                const int32_t* slot_mapping, int32_t num_tokens, int32_t row_elems, float inv_k,
                                float inv_v, hipStream_t stream);
 
-struct DecodeFp8Args {
-  void* out;  // bf16 [num_seqs, num_q_heads, 128]
-  const void* q;
-  const void* k_cache;  // fp8 codes [num_blocks, 256, num_kv_heads, 128]
-  const void* v_cache;
-  const int32_t* block_tables;
-  const int32_t* context_lens;
-  int32_t num_seqs;
-  int32_t num_q_heads;
-  int32_t num_kv_heads;
-  int32_t max_blocks_per_seq;
-  int32_t max_context_len;
-  int32_t blocks_per_chunk;  // 256-token blocks one workgroup streams (1, 2, 4, or a whole context of <= 32)
-  int32_t max_chunks;        // ceil(ceil(max_context_len / 256) / blocks_per_chunk): partials per sequence
-  float scale_log2;    // scale * k_scale * log2(e)
-  float v_scale;
-  float* part_ml;   // [num_seqs][max_chunks][num_q_heads][2]: reference max (log2 units) and sum
-  float* part_acc;  // [num_seqs][max_chunks][num_q_heads][128]: unnormalised outputs
-};
-
-// Blocks one fp8 decode workgroup streams (its chunk of a sequence's
-// context). With at least kF8WholeItems (sequence, query-head group) items,
-// a workgroup takes a whole context of up to kF8MaxChunkBlocks blocks: the
-// hardware dispatcher hands the next item to whichever CU frees a slot first,
-// which balances the uneven lengths, and no per-chunk start-up or merge is
-// paid more than once per item (on the Qwen3-8B-shaped workload, 256 x 8
-// items with 4-32 blocks each, whole contexts ran 504 us against 663 us for
-// 4-block chunks). Fewer items: 4 blocks while that still leaves at least
-// kF8MinItems workgroups for the largest contexts, else 2, else 1, so that
-// every CU gets work.
-constexpr int64_t kF8WholeItems = 512;
-constexpr int32_t kF8MaxChunkBlocks = 32;
-constexpr int64_t kF8MinItems = 4096;
-inline int32_t fp8_blocks_per_chunk(int64_t num_seqs, int64_t head_groups, int64_t max_blocks) {
-  if (num_seqs * head_groups >= kF8WholeItems)
-    return static_cast<int32_t>(max_blocks < kF8MaxChunkBlocks ? (max_blocks > 0 ? max_blocks : 1) : kF8MaxChunkBlocks);
-  for (int32_t bpc = 4; bpc > 1; bpc /= 2)
-    if (num_seqs * head_groups * ((max_blocks + bpc - 1) / bpc) >= kF8MinItems) return bpc;
-  return 1;
-}
-
-hipError_t launch_decode_fp8(const DecodeFp8Args& args, hipStream_t stream);
+// Decode over fp8 (E4M3) pools, head_dim 128, with the bf16/fp32 decode
+// kernel's work split and in-kernel merge: q and out bf16.
+hipError_t launch_decode_fp8_pools(const DecodeArgs& a, hipStream_t stream);
 
 
 // Grid the decode launcher uses when the caller does not fix one (`items` =
@@ -193,17 +155,6 @@ inline WorkspaceLayout make_workspace_layout(int64_t slot_rows, int64_t counters
   return w;
 }
 
-// Workspace of the fp8 decode: every (sequence, chunk, query head) partial
-// (sized by the caller for one-block chunks, the most partials).
-inline WorkspaceLayout decode_fp8_workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t max_chunks) {
-  WorkspaceLayout w;
-  const int64_t rows = num_seqs * max_chunks * num_q_heads;
-  w.lse_off = 0;
-  w.out_off = static_cast<size_t>((rows * 2 * 4 + 255) / 256 * 256);
-  w.counters_off = w.out_off + static_cast<size_t>(rows * 128 * 4);
-  w.total = w.counters_off;
-  return w;
-}
 
 // Decode: two piece slots per workgroup of the largest grid, each for up to
 // kDecodeMaxGroup query heads; one counter per (sequence, query head).

@@ -223,6 +223,8 @@ def test_fp8_validation():
     need = pa.decode_fp8_workspace_bytes(2, 8, 128, 1000)
     assert need == pa.decode_fp8_workspace_bytes(2, 8, 128, 1024) > 0
     assert pa.decode_fp8_workspace_bytes(2, 8, 64, 1000) == 0
+    # the fp8 decode shares the decode kernel and its workspace rule
+    assert need == pa.decode_workspace_bytes(2, 8, 128, 1000)
 
 
 def test_qknorm_rope_validation():

@@ -2,9 +2,9 @@
 quantising store bit for bit (including saturating and subnormal values and
 skipped slots), and decode attention over fp8 pools within the bf16 bar for
 GQA groups 1, 2 and 4, ragged contexts, NaN codes in every row no context
-covers, chunks of 1, 2 and 4 blocks and whole contexts (split past 32
-blocks), the Qwen3-0.6B-shaped decode workload at full size, and repeated runs
-bit-identical."""
+covers, batches from a few sequences to 480 and 512 (sequence, head-group)
+items with contexts up to 12000 tokens, the Qwen3-0.6B- and Qwen3-8B-shaped
+decode workloads at full size, and repeated runs bit-identical."""
 import numpy as np
 import pytest
 import torch
@@ -86,6 +86,17 @@ def test_one_token_context_returns_dequantised_v():
             assert torch.equal(out[i, g], want[g // 2].to(torch.float32).to(torch.bfloat16))
 
 
+def test_contexts_within_one_unit_need_no_workspace():
+    """Contexts of at most 64 tokens are never split, so the call needs no
+    workspace (the binding passes none)."""
+    scales = (0.0125, 0.02)
+    c, kq, vq = fp8_case(42, [1, 17, 64, 63], 16, 8, scales)
+    assert pa.decode_fp8_workspace_bytes(4, 16, 128, 64) == 0
+    out = run(c, kq, vq, scales)
+    ref = f8.paged_attn_decode_fp8(c.q, kq, vq, c.block_tables, c.context_lens, c.scale, *scales)
+    compare(out, ref, torch.bfloat16)
+
+
 def test_qwen3_0_6b_decode_workload_full_size():
     """Batch 64, 16 Q / 8 KV heads, contexts U[128, 4096], the pools of the
     bf16 workload quantised with scale 1/80."""
@@ -99,12 +110,12 @@ def test_qwen3_0_6b_decode_workload_full_size():
     compare(out, ref, torch.bfloat16, rows=seqs)
 
 
-@pytest.mark.parametrize("max_ctx,blocks", [(9216, 4), (4352, 2)], ids=["4blk", "2blk"])
-def test_decode_multi_block_chunks(max_ctx, blocks):
-    """60 sequences, 32 Q / 8 KV heads (480 items, too few for whole
-    contexts): contexts up to 9216 make the decode stream four blocks per
-    workgroup, up to 4352 two (the smaller tests run one-block chunks)."""
-    say(f"fp8 decode {blocks}-block chunks")
+@pytest.mark.parametrize("max_ctx,blocks", [(9216, 4), (4352, 2)], ids=["9216", "4352"])
+def test_decode_long_ragged_contexts(max_ctx, blocks):
+    """60 sequences, 32 Q / 8 KV heads (480 items), contexts uniform in
+    [1, max_ctx] with one of each extreme: many items split over several
+    workgroups and merged in the kernel."""
+    say(f"fp8 decode contexts up to {max_ctx}")
     rng = np.random.default_rng(77 + blocks)
     ctx = [int(x) for x in rng.integers(1, max_ctx, endpoint=True, size=60)]
     ctx[0], ctx[1] = max_ctx, 1
@@ -116,11 +127,11 @@ def test_decode_multi_block_chunks(max_ctx, blocks):
     compare(out, ref, torch.bfloat16, rows=seqs)
 
 
-def test_decode_whole_context_chunks():
-    """64 sequences x 8 query-head groups = 512 items: a workgroup takes a
-    whole context of up to 32 blocks, and the two longest contexts (47 and 33
-    blocks) are split into a 32-block chunk and a remainder."""
-    say("fp8 decode whole-context chunks")
+def test_decode_short_contexts_and_long_outliers():
+    """64 sequences x 8 query-head groups = 512 items, contexts up to 2000
+    tokens plus three of 12000, 8193 and 8192: the cost-balanced split gives
+    the outliers' items to several workgroups each."""
+    say("fp8 decode short contexts and long outliers")
     rng = np.random.default_rng(78)
     ctx = [int(x) for x in rng.integers(1, 2000, endpoint=True, size=64)]
     ctx[0], ctx[1], ctx[2] = 12000, 8193, 8192
@@ -136,8 +147,8 @@ def test_decode_whole_context_chunks():
 
 def test_qwen3_8b_shared_prefix_full_size_sampled():
     """The Qwen3-8B-shaped workload with a shared prefix at full size (batch
-    256, 32 Q / 8 KV heads, contexts U[1024, 8192]; whole-context chunks, as
-    the benchmark runs it): its bf16 pools quantised with scale 1/80 by torch
+    256, 32 Q / 8 KV heads, contexts U[1024, 8192], as the benchmark runs
+    it): its bf16 pools quantised with scale 1/80 by torch
     on the device (input generation), the oracle checks a sample of
     sequences, sharers and non-sharers, shortest and longest."""
     say("fp8 decode c4 full size")
