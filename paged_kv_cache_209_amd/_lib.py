@@ -147,13 +147,16 @@ def _dtype_code(t: torch.Tensor) -> int:
 _workspaces = {}
 
 
-def workspace(device: torch.device, nbytes: int, kind: str = "decode") -> Optional[torch.Tensor]:
-    """Zero-filled scratch for one entry point ("decode" or "prefill") on one
-    device. The two entry points lay their counters out differently, so they
-    never share a buffer."""
+def workspace(device: torch.device, nbytes: int, kind: str = "decode", stream: Optional[int] = None
+              ) -> Optional[torch.Tensor]:
+    """Zero-filled scratch for one entry point kind ("decode", "decode_fp8"
+    or "prefill") on one device and stream. The kinds lay their counters out
+    differently, so they never share a buffer; calls on different streams may
+    run at the same time, so each stream gets its own (the library's rule: one
+    workspace per stream of calls)."""
     if nbytes == 0:
         return None
-    key = (device.type, device.index, kind)
+    key = (device.type, device.index, kind, stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
@@ -237,7 +240,7 @@ def paged_attn_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Ten
             or block_tables.shape[0] != b or context_lens.shape != (b,):
         raise ValueError("paged_attn_decode_fp8: shapes do not match")
     need = decode_fp8_workspace_bytes(b, hq, d, max_context_len)
-    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need, kind="decode_fp8")
+    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need, "decode_fp8", _stream(q))
     ws_ptr = None if ws is None else ws.data_ptr()
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(library().pa_paged_attn_decode_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
@@ -295,7 +298,7 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     b, hq, d = q.shape
     nb, bs, hkv, _ = k_cache.shape
     need = decode_workspace_bytes(b, hq, d, max_context_len)
-    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need)
+    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need, "decode", _stream(q))
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     status = library().pa_paged_attn_decode_ex(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), b, hq, hkv, d, bs,
@@ -325,7 +328,7 @@ def paged_attn_decode_store(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
             or block_tables.shape[0] != b or context_lens.shape != (b,):
         raise ValueError("paged_attn_decode_store: shapes do not match")
     need = decode_workspace_bytes(b, hq, d, max_context_len)
-    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need)
+    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need, "decode", _stream(q))
     ws_ptr = None if ws is None else ws.data_ptr()
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(library().pa_paged_attn_decode_store(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new),
@@ -355,7 +358,7 @@ def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
     nb, bs, hkv, _ = k_cache.shape
     b = context_lens.shape[0]
     need = prefill_workspace_bytes(b, hq, d, max_q_len, max_context_len)
-    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need, "prefill")
+    ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need, "prefill", _stream(q))
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     status = library().pa_paged_attn_prefill(
         _ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),

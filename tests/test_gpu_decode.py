@@ -268,3 +268,27 @@ def test_zero_length_contexts_are_skipped(workgroups):
         assert torch.all(got[i] == 7.0)
     ref = oracle.paged_attn_decode(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.scale, seqs=[1, 3])
     compare(got, ref, torch.bfloat16, rows=[1, 3])
+
+
+def test_two_streams_concurrently():
+    """Two ragged batches decoded over and over on two streams at once
+    through the binding (each stream gets its own workspace): every result
+    is bit-identical to the same batch decoded alone."""
+    say("decode on two streams")
+    cases = [w.build_decode_case(f"streams{i}", ctx, 16, 8, 128, torch.bfloat16, 90 + i)
+             for i, ctx in enumerate(([3000, 65, 1, 2048, 700], [4096, 4000, 129, 10, 1500, 2222, 64]))]
+    dev = [dict(q=to_dev(c.q), kc=to_dev(c.k_cache), vc=to_dev(c.v_cache), bt=to_dev(c.block_tables),
+                cl=to_dev(c.context_lens)) for c in cases]
+    alone = [run_decode(c) for c in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty_like(d["q"]) for _ in range(4)] for d in dev]
+    torch.cuda.synchronize()
+    for r in range(4):
+        for i, (c, d) in enumerate(zip(cases, dev)):
+            with torch.cuda.stream(streams[i]):
+                pa.paged_attn_decode(outs[i][r], d["q"], d["kc"], d["vc"], d["bt"], d["cl"], c.scale,
+                                     c.max_context_len)
+    torch.cuda.synchronize()
+    for i in range(2):
+        for r in range(4):
+            assert torch.equal(bits(outs[i][r].cpu()), bits(alone[i].cpu())), (i, r)
