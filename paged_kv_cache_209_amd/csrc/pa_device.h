@@ -95,7 +95,7 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // DPP lane moves within a 16-lane row. Control codes: quad_perm(1,0,3,2),
-// quad_perm(2,3,0,1), row_half_mirror, row_ror:8.
+// quad_perm(2,3,0,1), row_half_mirror, row_ror:8, row_mirror.
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, true));
@@ -104,12 +104,21 @@ constexpr int kDppXor1 = 0xB1;
 constexpr int kDppXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowMirror = 0x140;
 
 // Sum over each aligned group of 8 lanes; every lane of the group gets it.
 __device__ __forceinline__ float sum8(float x) {
   x += dpp_f32<kDppXor1>(x);
   x += dpp_f32<kDppXor2>(x);
   x += dpp_f32<kDppHalfMirror>(x);
+  return x;
+}
+
+// Sum over each 16-lane row; every lane of the row gets it (the same
+// additions, in the same order, as a butterfly over lane bits 0 to 3).
+__device__ __forceinline__ float sum16(float x) {
+  x = sum8(x);
+  x += dpp_f32<kDppRowMirror>(x);
   return x;
 }
 

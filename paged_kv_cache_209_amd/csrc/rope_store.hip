@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kRopeWaves * kWave) void rope_kv_store_kernel(RopeS
 
   // Rotates the two P-element pieces (lo, hi) of one head row and writes them
   // to dst. With NORM the row is first divided by its root mean square (the
-  // 16 lanes of the head sum their squares by lane shuffles) and multiplied
+  // 16 lanes of the head, one DPP row, sum their squares) and multiplied
   // by the per-dimension weight (wlo, whi).
   auto rotate = [&](const V& lo, const V& hi, const V& wlo, const V& whi, T* dst) {
     float x[P], y[P];
@@ -122,8 +122,8 @@ __global__ __launch_bounds__(kRopeWaves * kWave) void rope_kv_store_kernel(RopeS
       float ss = 0.0f;
 #pragma unroll
       for (int e = 0; e < P; ++e) ss = fmaf(x[e], x[e], fmaf(y[e], y[e], ss));
-#pragma unroll
-      for (int off = 1; off < kLanesPerHead; off <<= 1) ss += __shfl_xor(ss, off, kWave);
+      static_assert(kLanesPerHead == 16, "a head's lanes are one 16-lane row");
+      ss = sum16(ss);  // DPP within the head's row of 16 lanes
       const float inv = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
 #pragma unroll
       for (int e = 0; e < P; ++e) {
