@@ -560,8 +560,8 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy --steps times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the paged-attention kernels run on a single device and this "
-              "build has no multi-GPU path (per-GPU work would be sharded by sequence or KV head with no "
+        print("bench.py measures one GPU only: the paged-attention kernels run on a single device and the "
+              "library has no multi-GPU path (per-GPU work would be sharded by sequence or KV head with no "
               "exchange). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

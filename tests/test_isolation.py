@@ -2,7 +2,7 @@
 sources never import or include anything of the oracle, the oracle never
 imports the package or includes its sources, importing the package loads no
 oracle module, and bench.py touches the oracle only inside its CPU-baseline
-functions."""
+functions. bench.py also refuses to run on more than one GPU."""
 import ast
 import os
 import re
@@ -72,3 +72,12 @@ def test_bench_uses_the_oracle_only_in_its_cpu_baseline():
                 if isinstance(sub, (ast.Import, ast.ImportFrom)):
                     mods = [a.name for a in sub.names] if isinstance(sub, ast.Import) else [sub.module or ""]
                     assert all(m.split(".")[0] != "oracle" for m in mods), f"{node.name} imports the oracle"
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says
+    so, before touching a device."""
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120, cwd=ROOT)
+    assert out.returncode == 2
+    assert "one GPU only" in out.stderr
