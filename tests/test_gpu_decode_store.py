@@ -5,6 +5,7 @@ last position. Checked against the oracle's kv_store followed by decode
 the same step issued as two launches (pa_kv_store then pa_paged_attn_decode),
 with NaN in every pool row no context covers, and with a skipped slot (the
 token still attends in flight but is not stored)."""
+import numpy as np
 import pytest
 import torch
 
@@ -92,3 +93,14 @@ def test_skipped_slot_attends_in_flight():
     hkv, d = c.k_cache.shape[2], c.k_cache.shape[3]
     flat = kc.cpu().reshape(-1, hkv, d)
     assert torch.equal(bits(flat[skipped]), bits(c.k_cache.reshape(-1, hkv, d)[skipped]))
+
+
+def test_more_sequences_than_workgroups():
+    """300 sequences (more than the 256-workgroup grid, so some workgroups
+    store two new rows), contexts 1 to 600 tokens."""
+    say("fused step 300 sequences")
+    rng = np.random.default_rng(303)
+    ctx = [int(x) for x in rng.integers(1, 600, endpoint=True, size=300)]
+    c = w.build_decode_case("fused300", ctx, 16, 8, 128, torch.bfloat16, 303)
+    assert pa.decode_num_workgroups(300, 16, 8, 128, c.max_context_len) < 300
+    check_case(c, torch.bfloat16)
