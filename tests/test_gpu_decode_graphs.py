@@ -133,3 +133,57 @@ def test_non_power_of_two_max_batch():
     with pytest.raises(pa.PagedAttnError):
         graphs.launch(13)
     graphs.close()
+
+
+def test_largest_bucket():
+    """max_batch 512 (the largest bucket the library captures): a step of 300
+    sequences runs the 512-bucket with 212 inert rows, so the graph's one
+    kernel stores up to two rows per workgroup; pools bit-exact, outputs
+    within the bf16 bar."""
+    say("decode graphs: max batch 512")
+    rng = np.random.default_rng(41)
+    gen = torch.Generator().manual_seed(41)
+    maxb, mb, nb = 512, 2, 700
+    n = 300
+    ctx = rng.integers(1, mb * BS, endpoint=True, size=n)
+    need = [-(-int(c) // BS) for c in ctx]
+    ids = rng.permutation(nb)[:sum(need)]
+    bt = np.full((n, mb), -1, dtype=np.int32)
+    slots = np.empty(n, dtype=np.int32)
+    k = 0
+    for i, c in enumerate(ctx):
+        bt[i, :need[i]] = ids[k:k + need[i]]
+        k += need[i]
+        slots[i] = bt[i, (c - 1) // BS] * BS + (c - 1) % BS
+    q = torch.randn((n, HQ, D), generator=gen).to(torch.bfloat16)
+    kn = torch.randn((n, HKV, D), generator=gen).to(torch.bfloat16)
+    vn = torch.randn((n, HKV, D), generator=gen).to(torch.bfloat16)
+    pool_k = torch.randn((nb, BS, HKV, D), generator=gen).to(torch.bfloat16)
+    pool_v = torch.randn((nb, BS, HKV, D), generator=gen).to(torch.bfloat16)
+    bufs = {
+        "out": torch.zeros((maxb, HQ, D), dtype=torch.bfloat16, device=DEV),
+        "q": torch.zeros((maxb, HQ, D), dtype=torch.bfloat16, device=DEV),
+        "k_new": torch.zeros((maxb, HKV, D), dtype=torch.bfloat16, device=DEV),
+        "v_new": torch.zeros((maxb, HKV, D), dtype=torch.bfloat16, device=DEV),
+        "slot_mapping": torch.full((maxb,), -1, dtype=torch.int32, device=DEV),
+        "block_tables": torch.full((maxb, mb), -1, dtype=torch.int32, device=DEV),
+        "context_lens": torch.zeros((maxb,), dtype=torch.int32, device=DEV),
+        "k_cache": pool_k.to(DEV),
+        "v_cache": pool_v.to(DEV),
+        "workspace": torch.zeros(pa.decode_workspace_bytes(maxb, HQ, D, mb * BS), dtype=torch.uint8, device=DEV),
+    }
+    graphs = DecodeGraphs(bufs, SCALE)
+    assert graphs.bucket(n) == 512 and graphs.bucket(512) == 512 and graphs.bucket(513) == 0
+    ctx_t = torch.from_numpy(ctx.astype(np.int32))
+    for name, t in (("q", q), ("k_new", kn), ("v_new", vn), ("slot_mapping", torch.from_numpy(slots)),
+                    ("block_tables", torch.from_numpy(bt)), ("context_lens", ctx_t)):
+        bufs[name][:n].copy_(t.to(DEV))
+    graphs.launch(n)
+    torch.cuda.synchronize()
+    kc, vc = oracle.kv_store(pool_k, pool_v, kn, vn, torch.from_numpy(slots))
+    assert torch.equal(bufs["k_cache"].cpu().view(torch.int16), kc.view(torch.int16))
+    assert torch.equal(bufs["v_cache"].cpu().view(torch.int16), vc.view(torch.int16))
+    seqs = list(range(0, n, 7))
+    ref = oracle.paged_attn_decode(q, kc, vc, torch.from_numpy(bt), ctx_t, SCALE, seqs=seqs)
+    compare(bufs["out"][:n], ref, torch.bfloat16, rows=seqs)
+    graphs.close()
