@@ -171,3 +171,25 @@ def test_qwen3_8b_shared_prefix_full_size_sampled():
     ref = f8.paged_attn_decode_fp8(c.q.cpu(), kq.cpu(), vq.cpu(), c.block_tables.cpu(), c.context_lens.cpu(), c.scale,
                                    s, s, seqs=seqs)
     compare(out, ref, torch.bfloat16, rows=seqs)
+
+
+def test_zero_length_contexts_are_skipped():
+    """A context length of 0 leaves that output row unwritten and does not
+    disturb the others."""
+    say("fp8 decode zero-length contexts")
+    scales = (0.0125, 0.02)
+    c, kq, vq = fp8_case(44, [1, 700, 1, 300, 1], 16, 8, scales, poison=False)
+    ctx = c.context_lens.clone()
+    ctx[0] = 0
+    ctx[2] = 0
+    ctx[4] = 0
+    q = to_dev(c.q)
+    out = torch.full_like(q, 7.0)
+    pa.paged_attn_decode_fp8(out, q, to_dev(kq), to_dev(vq), to_dev(c.block_tables), to_dev(ctx), c.scale,
+                             scales[0], scales[1], c.max_context_len)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    for i in (0, 2, 4):
+        assert torch.all(got[i] == 7.0)
+    ref = f8.paged_attn_decode_fp8(c.q, kq, vq, c.block_tables, c.context_lens, c.scale, *scales, seqs=[1, 3])
+    compare(got, ref, torch.bfloat16, rows=[1, 3])
