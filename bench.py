@@ -649,7 +649,7 @@ def main():
 
     if not args.skip_secondary and args.only in ("", "c4"):
         c4 = w.config4(device="cuda:0")
-        r4 = run_decode_workload(torch, pa, c4, max(5, args.steps // 5), 2, 1, with_store=False)
+        r4 = run_decode_workload(torch, pa, c4, max(20, args.steps // 2), 5, 1, with_store=False)
         db4 = decode_bytes(c4)
         ms = r4["decode_ms"]
         secondary["c4_qwen3_8b_decode_shared_prefix"] = {
@@ -683,7 +683,7 @@ def main():
         torch.cuda.empty_cache()
     if not args.skip_secondary and args.only in ("", "c5"):
         c5 = w.config5(device="cuda:0")
-        avg = run_prefill_workload(torch, pa, c5, max(5, args.steps // 5), 2, with_store=False)["prefill_ms"]
+        avg = run_prefill_workload(torch, pa, c5, max(20, args.steps // 2), 5, with_store=False)["prefill_ms"]
         fl = prefill_flops(c5)
         pb = prefill_bytes(c5)
         secondary["c5_spec_verify"] = {
@@ -703,7 +703,7 @@ def main():
         del c2f
         torch.cuda.empty_cache()
         c4f = w.config4(device="cuda:0")
-        fp8["c4_qwen3_8b_shared_prefix"] = run_fp8_decode(torch, pa, c4f, max(5, args.steps // 5), 1)
+        fp8["c4_qwen3_8b_shared_prefix"] = run_fp8_decode(torch, pa, c4f, max(20, args.steps // 2), 1)
         del c4f
         torch.cuda.empty_cache()
         secondary["fp8_kv_decode"] = fp8
