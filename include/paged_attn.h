@@ -45,12 +45,19 @@
  *   are undefined behaviour, not detected errors.
  * Threading. Calls are re-entrant. Calls that run concurrently (different
  *   streams) must not share a workspace.
- * Workspaces. Decode and prefill lay out their scratch differently: a
- *   workspace zero-filled once may be reused by any number of calls of ONE
- *   of the two entry points, whatever their sizes, never by both. (Partial
- *   results sit in fixed-size regions at the start; the counters follow at
- *   an offset that does not depend on the call's sizes, and every completed
- *   call leaves them zero.)
+ * Workspaces. The split-context calls keep partial results and 64-bit piece
+ *   counters in a caller workspace. Each counter word carries the tag of the
+ *   call that counts on it (a fresh epoch per call), and a call's first
+ *   arrival on a word raises it to that tag, so words left by any earlier
+ *   call -- completed, or abandoned part-way -- need no clearing between
+ *   calls. Zero-fill a workspace once before its first use: memory that was
+ *   never cleared may hold words above the call's tag, which the kernels
+ *   cannot reuse; such an item's output rows are then written as NaN (never
+ *   left stale, never merged from missing pieces) and the workspace's error
+ *   word is set, which pa_workspace_status reports as PA_ERR_WORKSPACE.
+ *   Decode and prefill lay out their scratch differently: one workspace
+ *   serves any number of calls of ONE of the two entry points, whatever
+ *   their sizes, never both.
  */
 #ifndef PAGED_ATTN_H_
 #define PAGED_ATTN_H_
@@ -66,7 +73,7 @@ typedef enum {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = -1, /* null pointer, non-positive or inconsistent size */
   PA_ERR_UNSUPPORTED = -2, /* valid but not built: dtype, head_dim, block_size */
-  PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  PA_ERR_WORKSPACE = -3,   /* workspace missing, too small, or found uncleared */
   PA_ERR_HIP = -4,         /* the HIP runtime reported a launch error */
   PA_ERR_NO_BLOCKS = -5    /* block manager: too few free blocks (preempt, retry) */
 } pa_status;
@@ -175,10 +182,9 @@ pa_status pa_qknorm_rope_kv_store(void* q_out, void* k_cache, void* v_cache, con
  *                max_blocks_per_seq * block_size.
  * scale        : multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
  * workspace    : device scratch of at least pa_decode_workspace_bytes(...)
- *                bytes for the split-context partial results. Its first use
- *                must see it zero-filled (e.g. from a zeroing allocation);
- *                every completed call leaves its counter words zero again, so
- *                the same workspace can be reused without clearing.
+ *                bytes for the split-context partial results, 16-byte
+ *                aligned, zero-filled once before its first use and then
+ *                reused without clearing (see Workspaces above).
  *                workspace may be NULL when max_context_len <= 64
  *                (pa_decode_workspace_bytes returns 0 then).
  * Supported dtypes: PA_F32, PA_BF16.
@@ -244,10 +250,11 @@ int32_t pa_decode_num_workgroups(int32_t num_seqs, int32_t num_q_heads, int32_t 
 
 /*
  * Workspace bytes that decode needs for these sizes with any number of
- * workgroups: one counter per (sequence, query head) plus two partial-result
- * slots per workgroup of the largest grid, so it does not grow with the
- * context length (0 when max_context_len <= 64, where nothing is ever
- * split). max_q_len is ignored (decode has one query token per sequence).
+ * workgroups: a 256-byte header, two partial-result slots per workgroup of
+ * the largest grid and one 8-byte counter per (sequence, query head), so it
+ * does not grow with the context length (0 when max_context_len <= 64,
+ * where nothing is ever split). max_q_len is ignored (decode has one query
+ * token per sequence).
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_q_len, int32_t max_context_len);
@@ -295,6 +302,19 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
                                   int32_t max_q_len, int32_t max_context_len);
 
 /*
+ * pa_workspace_status -- waits for the work queued on `stream`, then reads
+ * and clears the workspace's error word. PA_OK: no call since the last check
+ * met a counter it could not reuse. PA_ERR_WORKSPACE: some call did (the
+ * workspace was not zero-filled before its first use; the affected items'
+ * output rows hold NaN); zero-fill it and repeat those calls.
+ * PA_ERR_INVALID_ARG for a NULL workspace or one under 256 bytes; PA_ERR_HIP
+ * when the copy or the wait fails. Synchronises `stream`: a diagnostic, not
+ * for the hot path. Works for decode, fp8 decode, decode-graph and prefill
+ * workspaces alike.
+ */
+pa_status pa_workspace_status(void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
  * fp8 KV cache. The pages mention quantised KV-cache transfers ("Why
  * Understand Inference Engine Architecture?", Tensor Parallelism
  * Optimization, item 3) but fix no format. Reading taken: codes are OCP FP8
@@ -315,10 +335,10 @@ pa_status pa_kv_store_fp8(void* k_cache, void* v_cache, const void* k, const voi
                           float v_scale, pa_stream_t stream);
 
 /* Workspace bytes of pa_paged_attn_decode_fp8: the same as
- * pa_decode_workspace_bytes for these sizes, under the same rule (zero-filled
- * before the first call; every call leaves its counters zero; one workspace
- * per stream of calls). 0 when none is needed or the sizes are unsupported
- * (head_dim other than 128). */
+ * pa_decode_workspace_bytes for these sizes, under the same rules
+ * (zero-filled once before the first call; one workspace per stream of
+ * calls). 0 when none is needed or the sizes are unsupported (head_dim other
+ * than 128). */
 size_t pa_decode_fp8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                      int32_t max_context_len);
 
@@ -356,15 +376,16 @@ pa_status pa_paged_attn_decode_fp8(void* out, const void* q, const void* k_cache
  * pa_paged_attn_decode). Before each launch the caller writes the first
  * num_seqs rows of q, k_new, v_new, slot_mapping, block_tables and
  * context_lens. The launch then makes rows num_seqs .. bucket-1 inert
- * (slot -1: nothing stored; context 0: no output written) with a small
- * kernel on `stream`, and replays the bucket's graph on `stream`: out rows
+ * (slot -1: nothing stored; context 0: no output written) and writes the
+ * replay's piece-counter tag into the workspace header, with a small kernel
+ * on `stream`, and replays the bucket's graph on `stream`: out rows
  * 0 .. num_seqs-1 receive the step's attention. Contexts may be up to
  * max_blocks_per_seq * block_size tokens (the graphs are captured for that
- * bound). The workspace follows the decode rule (zero-filled before the first
- * launch, sized by pa_decode_workspace_bytes(max_batch, num_q_heads,
- * head_dim, 0, max_blocks_per_seq * block_size)); launches on one graph set
- * must not overlap. num_seqs > max_batch returns PA_ERR_INVALID_ARG (run
- * eagerly instead); num_seqs == 0 is a no-op.
+ * bound). The workspace (required; zero-filled before the first launch,
+ * sized by pa_decode_workspace_bytes(max_batch, num_q_heads, head_dim, 0,
+ * max_blocks_per_seq * block_size)) belongs to the graph set alone; launches
+ * on one graph set must not overlap. num_seqs > max_batch returns
+ * PA_ERR_INVALID_ARG (run eagerly instead); num_seqs == 0 is a no-op.
  */
 typedef struct pa_decode_graphs pa_decode_graphs;
 

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     PA_F32,
     PA_OK,
     PagedAttnError,
+    check_workspace,
     decode_fp8_workspace_bytes,
     decode_num_workgroups,
     decode_workspace_bytes,

@@ -54,6 +54,7 @@ SIGNATURES = {
     "pa_paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_workspace_status": (_i32, [_vp, _sz, _vp]),
     "pa_kv_store_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _vp]),
     "pa_decode_fp8_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "pa_paged_attn_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -140,8 +141,8 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 # ---------------------------------------------------------------------------
-# workspace: zero-filled once per device, reused (the kernels leave their
-# counter words zero at the end of every call)
+# workspace: zero-filled once per device, reused (the kernels tag their piece
+# counters per call, so nothing is cleared between calls)
 # ---------------------------------------------------------------------------
 
 _workspaces = {}
@@ -162,6 +163,18 @@ def workspace(device: torch.device, nbytes: int, kind: str = "decode", stream: O
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def check_workspace(ws: Optional[torch.Tensor]) -> None:
+    """pa_workspace_status: wait for the work queued on the current stream and
+    raise PagedAttnError(PA_ERR_WORKSPACE) if a call on `ws` met piece
+    counters it could not reuse (a workspace that was not zero-filled before
+    its first use; the affected output rows hold NaN). Clears the error word.
+    A diagnostic: it synchronises the stream."""
+    if ws is None:
+        return
+    _check(library().pa_workspace_status(_ptr(ws), ws.numel() * ws.element_size(), _stream(ws)),
+           "pa_workspace_status")
 
 
 # ---------------------------------------------------------------------------
@@ -291,12 +304,18 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     sequence's paged context. max_context_len is a host int >= every context
     length (no device sync is made to find it); num_workgroups = 0 lets the
     library choose how many workgroups share the work."""
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("paged_attn_decode: q [B, Hq, D] and pools [NB, 256, Hkv, D] expected")
+    b, hq, d = q.shape
+    nb, bs, hkv, dk = k_cache.shape
+    if out.shape != q.shape or dk != d or v_cache.shape != k_cache.shape or block_tables.dim() != 2 \
+            or block_tables.shape[0] != b or context_lens.shape != (b,):
+        raise ValueError("paged_attn_decode: shapes do not match (out == q [B, Hq, D], pools [NB, 256, Hkv, D], "
+                         "block_tables [B, *], context_lens [B])")
     for name, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _dev_tensor(t, name, q.dtype)
     _dev_tensor(block_tables, "block_tables", torch.int32)
     _dev_tensor(context_lens, "context_lens", torch.int32)
-    b, hq, d = q.shape
-    nb, bs, hkv, _ = k_cache.shape
     need = decode_workspace_bytes(b, hq, d, max_context_len)
     ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need, "decode", _stream(q))
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -350,13 +369,20 @@ def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
                        workspace_tensor: Optional[torch.Tensor] = None) -> torch.Tensor:
     """pa_paged_attn_prefill: causal attention of the new tokens (rows of q/k/v
     per cu_seqlens) over each sequence's cached blocks plus the new tokens."""
+    if q.dim() != 3 or k_cache.dim() != 4 or context_lens.dim() != 1:
+        raise ValueError("paged_attn_prefill: q [T, Hq, D], pools [NB, 256, Hkv, D], context_lens [B] expected")
+    total_q, hq, d = q.shape
+    nb, bs, hkv, dk = k_cache.shape
+    b = context_lens.shape[0]
+    if out.shape != q.shape or dk != d or v_cache.shape != k_cache.shape or k.shape != (total_q, hkv, d) \
+            or v.shape != k.shape or block_tables.dim() != 2 or block_tables.shape[0] != b \
+            or cu_seqlens.shape != (b + 1,):
+        raise ValueError("paged_attn_prefill: shapes do not match (out == q [T, Hq, D], k/v [T, Hkv, D], pools "
+                         "[NB, 256, Hkv, D], block_tables [B, *], context_lens [B], cu_seqlens [B + 1])")
     for name, t in (("out", out), ("q", q), ("k", k), ("v", v), ("k_cache", k_cache), ("v_cache", v_cache)):
         _dev_tensor(t, name, q.dtype)
     for name, t in (("block_tables", block_tables), ("context_lens", context_lens), ("cu_seqlens", cu_seqlens)):
         _dev_tensor(t, name, torch.int32)
-    total_q, hq, d = q.shape
-    nb, bs, hkv, _ = k_cache.shape
-    b = context_lens.shape[0]
     need = prefill_workspace_bytes(b, hq, d, max_q_len, max_context_len)
     ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need, "prefill", _stream(q))
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()

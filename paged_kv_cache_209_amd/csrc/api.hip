@@ -5,9 +5,37 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
 
 #include "paged_attn.h"
 #include "pa_launch.h"
+
+namespace pa {
+
+// Epochs of the piece-counter tags: one process-wide sequence, started at a
+// random point below 2^47 (so that memory left by another process that used
+// this library is unlikely to hold a tag of ours, and 2^47 calls fit before
+// the 48-bit field would wrap).
+uint64_t next_epoch_tag() {
+  static std::atomic<uint64_t> next{[] {
+    uint64_t x = static_cast<uint64_t>(std::chrono::high_resolution_clock::now().time_since_epoch().count());
+    x ^= static_cast<uint64_t>(getpid()) << 32;
+    x ^= reinterpret_cast<uintptr_t>(&x);
+    // splitmix64 finaliser (mixes every input bit into every output bit)
+    x += 0x9E3779B97F4A7C15ull;
+    x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+    x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+    x ^= x >> 31;
+    return (x & ((uint64_t{1} << 46) - 1)) + 1;
+  }()};
+  const uint64_t epoch = next.fetch_add(1, std::memory_order_relaxed) & ((uint64_t{1} << 48) - 1);
+  return (epoch == 0 ? 1 : epoch) << 16;
+}
+
+}  // namespace pa
 
 namespace {
 
@@ -66,7 +94,7 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_UNSUPPORTED:
       return "PA_ERR_UNSUPPORTED: unsupported dtype, head_dim or block_size";
     case PA_ERR_WORKSPACE:
-      return "PA_ERR_WORKSPACE: workspace missing or too small";
+      return "PA_ERR_WORKSPACE: workspace missing, too small, or not zero-filled before its first use";
     case PA_ERR_HIP:
       return "PA_ERR_HIP: HIP runtime error";
     case PA_ERR_NO_BLOCKS:
@@ -182,6 +210,21 @@ pa_status pa_qknorm_rope_kv_store(void* q_out, void* k_cache, void* v_cache, con
 
 namespace {
 
+// Points the decode arguments at the workspace's regions (all null when the
+// call splits nothing) and gives the call its counter tag: a fresh one, or,
+// for graph replays, the tag the replay's set-up kernel writes into the
+// workspace header (`epoch_word`).
+void set_decode_workspace(pa::DecodeArgs& a, void* workspace, const pa::WorkspaceLayout& lay,
+                          const uint64_t* epoch_word) {
+  char* ws = static_cast<char*>(workspace);
+  a.counters = ws ? reinterpret_cast<uint64_t*>(ws + lay.counters_off) : nullptr;
+  a.ws_flags = ws ? reinterpret_cast<uint32_t*>(ws + pa::kWorkspaceFlagsOff) : nullptr;
+  a.part_lse = ws ? reinterpret_cast<float*>(ws + lay.lse_off) : nullptr;
+  a.part_out = ws ? reinterpret_cast<float*>(ws + lay.out_off) : nullptr;
+  a.epoch_tag = pa::next_epoch_tag();
+  a.epoch_word = ws ? epoch_word : nullptr;
+}
+
 // Decode, optionally fused with the store of the step's new K/V rows
 // (k_new non-null: k_new, v_new [num_seqs, num_kv_heads, head_dim] and
 // slot_mapping [num_seqs]).
@@ -190,7 +233,8 @@ pa_status decode_common(void* out, const void* q, const void* k_cache, const voi
                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                         int32_t max_context_len, float scale, pa_dtype dtype, int32_t num_workgroups,
-                        void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+                        void* workspace, size_t workspace_bytes, pa_stream_t stream,
+                        const uint64_t* epoch_word = nullptr) {
   if (num_seqs < 0 || num_q_heads <= 0) return PA_ERR_INVALID_ARG;
   const pa_status st = check_common(num_kv_heads, head_dim, block_size, num_blocks, dtype);
   if (st != PA_OK) return st;
@@ -230,10 +274,7 @@ pa_status decode_common(void* out, const void* q, const void* k_cache, const voi
   a.max_units = decode_max_units(num_seqs, num_q_heads, num_kv_heads, max_context_len);
   a.scale_log2 = scale * kLog2e;
   a.v_scale = 1.0f;
-  char* ws = static_cast<char*>(workspace);
-  a.counters = split ? reinterpret_cast<int32_t*>(ws + lay.counters_off) : nullptr;
-  a.part_lse = split ? reinterpret_cast<float*>(ws + lay.lse_off) : nullptr;
-  a.part_out = split ? reinterpret_cast<float*>(ws + lay.out_off) : nullptr;
+  set_decode_workspace(a, split ? workspace : nullptr, lay, epoch_word);
   a.k_new = k_new;
   a.v_new = v_new;
   a.slot_mapping = slot_mapping;
@@ -268,6 +309,21 @@ pa_status pa_paged_attn_decode_store(void* out, const void* q, void* k_cache, vo
   return decode_common(out, q, k_cache, v_cache, num_seqs > 0 ? k_new : nullptr, v_new, slot_mapping, block_tables,
                        context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, max_context_len, scale, dtype, 0, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_workspace_status(void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  if (workspace == nullptr || workspace_bytes < pa::kWorkspaceHeaderBytes) return PA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* word = static_cast<char*>(workspace) + pa::kWorkspaceFlagsOff;
+  uint32_t flags = 0;
+  (void)hipGetLastError();
+  if (hipMemcpyAsync(&flags, word, sizeof(flags), hipMemcpyDeviceToHost, s) != hipSuccess) return PA_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return PA_ERR_HIP;
+  if (flags == 0) return PA_OK;
+  static const uint32_t kZero = 0;
+  if (hipMemcpyAsync(word, &kZero, sizeof(kZero), hipMemcpyHostToDevice, s) != hipSuccess) return PA_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return PA_ERR_HIP;
+  return PA_ERR_WORKSPACE;
 }
 
 pa_status pa_paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -347,10 +403,7 @@ pa_status pa_paged_attn_decode_fp8(void* out, const void* q, const void* k_cache
   a.max_units = decode_max_units(num_seqs, num_q_heads, num_kv_heads, max_context_len);
   a.scale_log2 = scale * k_scale * kLog2e;
   a.v_scale = v_scale;
-  char* ws = static_cast<char*>(workspace);
-  a.counters = split ? reinterpret_cast<int32_t*>(ws + lay.counters_off) : nullptr;
-  a.part_lse = split ? reinterpret_cast<float*>(ws + lay.lse_off) : nullptr;
-  a.part_out = split ? reinterpret_cast<float*>(ws + lay.out_off) : nullptr;
+  set_decode_workspace(a, split ? workspace : nullptr, lay, nullptr);
   a.k_new = nullptr;
   a.v_new = nullptr;
   a.slot_mapping = nullptr;
@@ -430,7 +483,9 @@ pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const v
   a.rows_per_tile = rows;
   a.num_workgroups = static_cast<int32_t>(max_units < cap ? max_units : cap);
   char* ws = static_cast<char*>(workspace);
-  a.counters = reinterpret_cast<int32_t*>(ws + lay.counters_off);
+  a.counters = reinterpret_cast<uint64_t*>(ws + lay.counters_off);
+  a.ws_flags = reinterpret_cast<uint32_t*>(ws + pa::kWorkspaceFlagsOff);
+  a.epoch_tag = pa::next_epoch_tag();
   a.part_lse = reinterpret_cast<float*>(ws + lay.lse_off);
   a.part_out = reinterpret_cast<float*>(ws + lay.out_off);
   (void)hipGetLastError();
@@ -438,3 +493,24 @@ pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const v
 }
 
 }  // extern "C"
+
+namespace pa {
+
+pa_status decode_store_for_graph(void* out, const void* q, void* k_cache, void* v_cache, const void* k_new,
+                                 const void* v_new, const int32_t* slot_mapping, const int32_t* block_tables,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
+                                 void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  if (num_seqs > 0 && (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr)) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!aligned16(k_new) || !aligned16(v_new))) return PA_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < kWorkspaceHeaderBytes) return PA_ERR_WORKSPACE;
+  const uint64_t* epoch_word =
+      reinterpret_cast<const uint64_t*>(static_cast<const char*>(workspace) + kWorkspaceEpochOff);
+  return decode_common(out, q, k_cache, v_cache, num_seqs > 0 ? k_new : nullptr, v_new, slot_mapping, block_tables,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, max_context_len, scale, dtype, 0, workspace, workspace_bytes, stream,
+                       epoch_word);
+}
+
+}  // namespace pa

@@ -861,23 +861,40 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
   // each wave counts its own share, and an item is complete at kDecodeWaves
   // counts per piece. The wave whose count completes an item merges its
   // pieces in piece order, so the result does not depend on timing.
+  //
+  // Ordering this relies on (gfx950): the pieces' partials are agent-scope
+  // stores, which write through to the device-coherent level, and a wave's
+  // vector-memory counter covers stores until that level has acknowledged
+  // them, so after the wait each stored partial is visible to every XCD
+  // before the count that announces it is issued. The merging wave issues its
+  // agent-scope loads (which bypass the non-coherent caches) only after its
+  // count has returned. The write-back and invalidate a release/acquire pair
+  // would add cover plain cached accesses, which the partials never use.
   if (pend_item[0] >= 0) {
     wait_vector_memory();
-    // lanes 0 and 1 count the two pieces with one instruction
+    // lanes 0 and 1 count the two pieces together
     const int mine_item = lane == 0 ? pend_item[0] : pend_item[1];
+    const uint64_t tag = a.epoch_word != nullptr ? __hip_atomic_load(const_cast<uint64_t*>(a.epoch_word),
+                                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                                 : a.epoch_tag;
     int t = 0;
-    if (lane < 2 && mine_item >= 0) t = add_agent(a.counters + mine_item, 1);
-    const int t0 = __builtin_amdgcn_readlane(t, 0);
-    const int t1 = __builtin_amdgcn_readlane(t, 1);
-    if (t0 == kDecodeWaves * pend_n[0] - 1) {
-      merge_item<IoT, D, GT, kOutScale>(a, out, pend_unit0[0], split, pend_first[0], pend_n[0], pend_item_first[0],
-                                        lane);
-      if (lane == 0) store_agent_int(a.counters + pend_item[0], 0);
-    }
-    if (pend_item[1] >= 0 && t1 == kDecodeWaves * pend_n[1] - 1) {
-      merge_item<IoT, D, GT, kOutScale>(a, out, pend_unit0[1], split, pend_first[1], pend_n[1], pend_item_first[1],
-                                        lane);
-      if (lane == 0) store_agent_int(a.counters + pend_item[1], 0);
+    if (lane < 2 && mine_item >= 0) t = count_arrival(a.counters + mine_item, tag);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int tk = __builtin_amdgcn_readlane(t, k);
+      if (pend_item[k] < 0) continue;
+      const int expected = kDecodeWaves * pend_n[k];
+      if (tk == expected) {
+        merge_item<IoT, D, GT, kOutScale>(a, out, pend_unit0[k], split, pend_first[k], pend_n[k],
+                                          pend_item_first[k], lane);
+      } else if (tk < 0 || tk > expected) {
+        // A counter that was not this call's (never-cleared workspace): the
+        // pieces cannot be trusted, so the item's rows are set to NaN and the
+        // error word tells the caller.
+        if (lane == 0) flag_workspace(a.ws_flags, kWorkspaceErrStaleCounter);
+        for (int o = lane; o < GT * D; o += kWave)
+          store_out<IoT>(out + pend_unit0[k] * D + o, __builtin_nanf(""));
+      }
     }
   }
 }

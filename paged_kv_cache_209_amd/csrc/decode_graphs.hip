@@ -6,8 +6,10 @@
 // sequences runs the smallest bucket that holds it; the rows between n and the
 // bucket are made inert first (slot -1 stores nothing, context 0 writes no
 // output), by a small kernel launched outside the graph on the caller's
-// stream. Nothing inside the graphs clears memory: the decode workspace keeps
-// its own rule (counters left zero by every call).
+// stream before every replay; the same kernel writes the replay's fresh
+// piece-counter tag into the workspace header, where the captured decode
+// reads it (a captured launch keeps its capture-time arguments). Nothing
+// inside the graphs clears memory.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -15,13 +17,17 @@
 #include <vector>
 
 #include "paged_attn.h"
+#include "pa_launch.h"
 
 namespace {
 
 constexpr int32_t kMaxGraphBatch = 512;
 
-__global__ void make_rows_inert(int32_t* slot_mapping, int32_t* context_lens, int32_t from, int32_t to) {
-  const int32_t i = from + static_cast<int32_t>(blockIdx.x * blockDim.x + threadIdx.x);
+__global__ void make_rows_inert(int32_t* slot_mapping, int32_t* context_lens, int32_t from, int32_t to,
+                                uint64_t* epoch_word, uint64_t tag) {
+  const int32_t t = static_cast<int32_t>(blockIdx.x * blockDim.x + threadIdx.x);
+  if (t == 0 && epoch_word != nullptr) __hip_atomic_store(epoch_word, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int32_t i = from + t;
   if (i < to) {
     slot_mapping[i] = -1;
     context_lens[i] = 0;
@@ -101,7 +107,7 @@ pa_status pa_decode_graphs_create(const pa_decode_graph_buffers* bufs, int32_t m
       break;
     }
     // one kernel node: the store of the new rows fused with the decode
-    const pa_status s2 = pa_paged_attn_decode_store(
+    const pa_status s2 = pa::decode_store_for_graph(
         bufs->out, bufs->q, bufs->k_cache, bufs->v_cache, bufs->k_new, bufs->v_new, bufs->slot_mapping,
         bufs->block_tables, bufs->context_lens, b, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
         max_blocks_per_seq, max_ctx, scale, dtype, bufs->workspace, bufs->workspace_bytes, cap);
@@ -145,12 +151,14 @@ pa_status pa_decode_graphs_launch(pa_decode_graphs* g, int32_t num_seqs, pa_stre
   const int32_t bucket = g->buckets[k];
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (bucket > num_seqs) {
-    const int32_t n = bucket - num_seqs;
-    make_rows_inert<<<dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s>>>(
-        g->bufs.slot_mapping, g->bufs.context_lens, num_seqs, bucket);
-    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-  }
+  // every replay: the padding rows (if any) and the replay's counter tag
+  const int32_t n = bucket - num_seqs;
+  uint64_t* epoch_word =
+      g->bufs.workspace ? reinterpret_cast<uint64_t*>(static_cast<char*>(g->bufs.workspace) + pa::kWorkspaceEpochOff)
+                        : nullptr;
+  make_rows_inert<<<dim3(static_cast<uint32_t>(n > 0 ? (n + 255) / 256 : 1)), dim3(256), 0, s>>>(
+      g->bufs.slot_mapping, g->bufs.context_lens, num_seqs, bucket, epoch_word, pa::next_epoch_tag());
+  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   return hipGraphLaunch(g->execs[k], s) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

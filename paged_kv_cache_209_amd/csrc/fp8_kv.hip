@@ -20,7 +20,24 @@ namespace pa {
 
 namespace {
 
+// Saturation to the largest finite E4M3 magnitude (infinities included).
+// fminf/fmaxf return the non-NaN operand, so a NaN would come out as -448:
+// NaNs are given their code separately (nan_fixup).
 __device__ __forceinline__ float clamp_fp8(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
+
+// Replaces the code of every NaN among the four values packed into w (value
+// b in byte b) by the E4M3 NaN pattern with the value's sign, S.1111.111.
+__device__ __forceinline__ uint32_t nan_fixup(uint32_t w, float x0, float x1, float x2, float x3) {
+  const float xs[4] = {x0, x1, x2, x3};
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (xs[b] != xs[b]) {
+      const uint32_t code = 0x7Fu | ((__float_as_uint(xs[b]) >> 31) << 7);
+      w = (w & ~(0xFFu << (8 * b))) | (code << (8 * b));
+    }
+  }
+  return w;
+}
 
 // Quantising store: one thread per 8 elements of a token's [Hkv, D] row of K
 // and the same of V.
@@ -43,16 +60,16 @@ __global__ __launch_bounds__(256) void kv_store_fp8_kernel(uint8_t* __restrict__
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     // bf16 words 2h and 2h+1 hold elements 4h .. 4h+3
-    int wk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fp8(bf16_lo(kk[2 * h]) * inv_k),
-                                             clamp_fp8(bf16_hi(kk[2 * h]) * inv_k), 0, false);
-    wk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fp8(bf16_lo(kk[2 * h + 1]) * inv_k),
-                                         clamp_fp8(bf16_hi(kk[2 * h + 1]) * inv_k), wk, true);
-    int wv = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fp8(bf16_lo(vv[2 * h]) * inv_v),
-                                             clamp_fp8(bf16_hi(vv[2 * h]) * inv_v), 0, false);
-    wv = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fp8(bf16_lo(vv[2 * h + 1]) * inv_v),
-                                         clamp_fp8(bf16_hi(vv[2 * h + 1]) * inv_v), wv, true);
-    kw[h] = static_cast<uint32_t>(wk);
-    vw[h] = static_cast<uint32_t>(wv);
+    const float k0 = bf16_lo(kk[2 * h]) * inv_k, k1 = bf16_hi(kk[2 * h]) * inv_k;
+    const float k2 = bf16_lo(kk[2 * h + 1]) * inv_k, k3 = bf16_hi(kk[2 * h + 1]) * inv_k;
+    const float v0 = bf16_lo(vv[2 * h]) * inv_v, v1 = bf16_hi(vv[2 * h]) * inv_v;
+    const float v2 = bf16_lo(vv[2 * h + 1]) * inv_v, v3 = bf16_hi(vv[2 * h + 1]) * inv_v;
+    int wk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fp8(k0), clamp_fp8(k1), 0, false);
+    wk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fp8(k2), clamp_fp8(k3), wk, true);
+    int wv = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fp8(v0), clamp_fp8(v1), 0, false);
+    wv = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fp8(v2), clamp_fp8(v3), wv, true);
+    kw[h] = nan_fixup(static_cast<uint32_t>(wk), k0, k1, k2, k3);
+    vw[h] = nan_fixup(static_cast<uint32_t>(wv), v0, v1, v2, v3);
   }
   const int64_t dst = (static_cast<int64_t>(slot) * pieces_per_row + piece) * 8;
   uint2 ko, vo;

@@ -169,6 +169,23 @@ __device__ __forceinline__ int add_agent(int* p, int v) {
 __device__ __forceinline__ void store_agent_int(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// One arrival on a tagged piece counter (the workspace layout describes the
+// tags): raise the word to the call's tag, then add one. Both atomics go to
+// the same word from the same lane, so they take effect in program order.
+// Returns the count after this arrival, or -1 when the word holds a foreign
+// tag above the call's own (never-cleared memory).
+__device__ __forceinline__ int count_arrival(uint64_t* ctr, uint64_t tag) {
+  __hip_atomic_fetch_max(ctr, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t old = __hip_atomic_fetch_add(ctr, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((old >> 16) != (tag >> 16)) return -1;
+  return static_cast<int>(old & 0xFFFFu) + 1;
+}
+
+// Sets error bits in the workspace's error word.
+__device__ __forceinline__ void flag_workspace(uint32_t* flags, uint32_t bits) {
+  __hip_atomic_fetch_or(flags, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // 16-byte agent-coherent accesses through a raw buffer descriptor (cache
 // policy sc1): the descriptor covers `bytes` bytes from `base` (out-of-range
 // offsets read 0 and drop writes).

@@ -261,10 +261,12 @@ __device__ __forceinline__ void issue_tile(TileSrc<D, NT, KT>& t, int kt, char* 
 // 2 first_owner + 1 for the first piece when its owner's range starts inside
 // an earlier item. Each thread takes 4 dims of kRowsPerThread rows and keeps
 // the loads of kMergeBatch pieces of a group of rows in flight together.
+// With `poison` (the item's counter held another call's tag, so its pieces
+// cannot be trusted) the rows are written as NaN instead.
 template <int D, int ROWS, int NT>
 __device__ __forceinline__ void merge_pieces(const PrefillArgs& a, bf16_t* outp, int64_t first_owner, int n_parts,
                                              bool first_in_late_slot, const SeqGeom& sg, int qt, int h, int group,
-                                             int tid) {
+                                             int tid, bool poison) {
   constexpr int D4 = D / 4;
   constexpr int kRowStep = NT / D4;
   constexpr int kRowsPerThread = ROWS / kRowStep;
@@ -273,6 +275,17 @@ __device__ __forceinline__ void merge_pieces(const PrefillArgs& a, bf16_t* outp,
   static_assert(ROWS % kRowStep == 0 && kRowsPerThread % kRowGroup == 0, "merge tiling");
   const int d4 = tid % D4;
   const int r0 = tid / D4;
+  if (poison) {
+    const uint32_t nan2 = pack_bf16x2(__builtin_nanf(""), __builtin_nanf(""));
+    for (int k = 0; k < kRowsPerThread; ++k) {
+      const int R = qt * ROWS + r0 + k * kRowStep;
+      const int j = R / group;
+      if (j >= sg.n) continue;
+      bf16_t* orow = outp + (static_cast<int64_t>(sg.start + j) * a.num_q_heads + h * group + R % group) * D;
+      *reinterpret_cast<uint2*>(orow + 4 * d4) = make_uint2(nan2, nan2);
+    }
+    return;
+  }
   for (int rg = 0; rg < kRowsPerThread; rg += kRowGroup) {
     float m[kRowGroup], den[kRowGroup];
     f32x4_t num[kRowGroup];
@@ -756,25 +769,26 @@ __global__ __launch_bounds__(64 * WM, prefill_workgroups_per_cu<WM>()) void page
     wait_vector_memory();
     __syncthreads();
     const int64_t qtiles_max = (static_cast<int64_t>(a.max_q_len) * group + ROWS - 1) / ROWS;
-    if (tid < 2) {  // threads 0 and 1 count the two pieces
+    if (tid < 2) {  // threads 0 and 1 count the two pieces (tagged counters, see pa_launch.h)
       const int n = tid == 0 ? pend_n[0] : pend_n[1];
-      int last = 0;
+      int state = 0;  // 1: this arrival completes the item; -1: foreign counter
       if (n > 0) {
         const int64_t item = static_cast<int64_t>(tid == 0 ? pend_seq[0] : pend_seq[1]) * Hkv +
                              (tid == 0 ? pend_h[0] : pend_h[1]);
-        int* ctr = a.counters + item * qtiles_max + (tid == 0 ? pend_qt[0] : pend_qt[1]);
-        last = add_agent(ctr, 1) == n - 1;
-        if (last) store_agent_int(ctr, 0);
+        uint64_t* ctr = a.counters + item * qtiles_max + (tid == 0 ? pend_qt[0] : pend_qt[1]);
+        const int cnt = count_arrival(ctr, a.epoch_tag);
+        state = cnt == n ? 1 : (cnt < 0 || cnt > n ? -1 : 0);
+        if (state < 0) flag_workspace(a.ws_flags, kWorkspaceErrStaleCounter);
       }
-      s_cnt[tid] = last;
+      s_cnt[tid] = state;
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      if (pend_n[k] > 0 && s_cnt[k]) {
+      if (pend_n[k] > 0 && s_cnt[k] != 0) {
         const bool late = pend_first[k] * U / G < pend_item_first[k];
         merge_pieces<D, ROWS, NT>(a, outp, pend_first[k], pend_n[k], late, seq_geom(a, pend_seq[k]), pend_qt[k],
-                                  pend_h[k], group, tid);
+                                  pend_h[k], group, tid, s_cnt[k] < 0);
       }
     }
   }

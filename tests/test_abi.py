@@ -265,3 +265,79 @@ def test_decode_store_validation():
     assert fused(d=80) == UNSUP
     assert fused(ws=None, wsb=0) == WS
     assert fused(B=0, out=None, q=None, kn=None, vn=None, sl=None, bt=None, cl=None) == pa.PA_OK
+
+
+def test_workspace_status_validation():
+    """pa_workspace_status rejects a missing or headerless workspace before
+    any HIP call (it is a diagnostic that synchronises the stream)."""
+    lib = pa.library()
+    assert lib.pa_workspace_status(None, 1 << 20, None) == INVALID
+    assert lib.pa_workspace_status(P, 255, None) == INVALID
+    pa.check_workspace(None)  # no workspace: nothing to check
+
+
+def test_workspace_layout_has_header_and_wide_counters():
+    """Decode: 256-byte header, partial regions for the largest grid, then
+    8 bytes per (sequence, query head); prefill likewise per counter."""
+    a = pa.decode_workspace_bytes(4, 8, 128, 65)
+    b = pa.decode_workspace_bytes(5, 8, 128, 65)
+    assert b - a == 8 * 8
+    assert a >= 256 + 2 * 2048 * 4 * (128 + 1) * 4 + 4 * 8 * 8
+    p1 = pa.prefill_workspace_bytes(2, 8, 128, 5, 4096)
+    p2 = pa.prefill_workspace_bytes(3, 8, 128, 5, 4096)
+    assert p2 - p1 == 8 * 8 * 6
+
+
+def _cpu(shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _decode_args(**kw):
+    a = dict(out=_cpu((4, 8, 128)), q=_cpu((4, 8, 128)), kc=_cpu((3, 256, 2, 128)), vc=_cpu((3, 256, 2, 128)),
+             bt=_cpu((4, 2), torch.int32), cl=_cpu((4,), torch.int32))
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("kw", [
+    dict(out=_cpu((4, 8, 64))), dict(out=_cpu((3, 8, 128))), dict(q=_cpu((4, 8, 64)), out=_cpu((4, 8, 64))),
+    dict(vc=_cpu((4, 256, 2, 128))), dict(bt=_cpu((3, 2), torch.int32)), dict(bt=_cpu((4,), torch.int32)),
+    dict(cl=_cpu((5,), torch.int32)), dict(q=_cpu((4, 1024))),
+], ids=["out_d", "out_b", "q_d_vs_pool", "pools_differ", "bt_rows", "bt_1d", "cl_len", "q_2d"])
+def test_decode_binding_rejects_mismatched_shapes(kw):
+    a = _decode_args(**kw)
+    with pytest.raises(ValueError, match="paged_attn_decode"):
+        pa.paged_attn_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], 0.1, 512)
+
+
+def test_decode_binding_shapes_pass_then_device_check():
+    a = _decode_args()
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pa.paged_attn_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], 0.1, 512)
+
+
+def _prefill_args(**kw):
+    a = dict(out=_cpu((10, 8, 128)), q=_cpu((10, 8, 128)), k=_cpu((10, 2, 128)), v=_cpu((10, 2, 128)),
+             kc=_cpu((3, 256, 2, 128)), vc=_cpu((3, 256, 2, 128)), bt=_cpu((2, 2), torch.int32),
+             cl=_cpu((2,), torch.int32), cu=_cpu((3,), torch.int32))
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("kw", [
+    dict(out=_cpu((9, 8, 128))), dict(k=_cpu((10, 4, 128))), dict(v=_cpu((9, 2, 128))),
+    dict(q=_cpu((10, 8, 64)), out=_cpu((10, 8, 64))), dict(vc=_cpu((3, 256, 1, 128))),
+    dict(bt=_cpu((3, 2), torch.int32)), dict(cu=_cpu((2,), torch.int32)), dict(cl=_cpu((2, 1), torch.int32)),
+], ids=["out_rows", "k_heads", "v_rows", "q_d_vs_pool", "pools_differ", "bt_rows", "cu_len", "cl_2d"])
+def test_prefill_binding_rejects_mismatched_shapes(kw):
+    a = _prefill_args(**kw)
+    with pytest.raises(ValueError, match="paged_attn_prefill"):
+        pa.paged_attn_prefill(a["out"], a["q"], a["k"], a["v"], a["kc"], a["vc"], a["bt"], a["cl"], a["cu"], 0.1,
+                              5, 512)
+
+
+def test_prefill_binding_shapes_pass_then_device_check():
+    a = _prefill_args()
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pa.paged_attn_prefill(a["out"], a["q"], a["k"], a["v"], a["kc"], a["vc"], a["bt"], a["cl"], a["cu"], 0.1,
+                              5, 512)

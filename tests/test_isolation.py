@@ -62,7 +62,7 @@ def test_importing_the_package_loads_no_oracle_module():
 def test_bench_uses_the_oracle_only_in_its_cpu_baseline():
     path = os.path.join(ROOT, "bench.py")
     tree = ast.parse(open(path).read(), path)
-    allowed = {"cpu_baseline", "block_manager_oracle_step_us"}
+    allowed = {"cpu_baseline", "cpu_baseline_prefill", "block_manager_oracle_step_us"}
     for node in tree.body:
         if isinstance(node, (ast.Import, ast.ImportFrom)):
             mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module or ""]

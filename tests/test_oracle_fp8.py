@@ -74,11 +74,48 @@ def test_quantizer_is_nearest_even():
 
 
 def test_quantizer_scale_uses_fp32_reciprocal():
-    x = torch.tensor([0.3, -1.7, 5.0, 1e-3], dtype=torch.float32)
-    s = 0.037
-    inv = np.float32(1.0) / np.float32(s)
-    y = torch.tensor(np.float32(x.numpy() * inv))
-    assert torch.equal(f8.quantize(x, s), f8.quantize(y, 1.0))
+    """A value where the reading (1/s formed in fp32, the product rounded to
+    fp32, then the nearest code) and exact division disagree, worked by hand.
+    s = 0.7 is held as the fp32 0.699999988079071044921875; its fp32
+    reciprocal is 1.4285714626312255859375. For x = -17.5 the product
+    -25.00000059604644775390625 rounds to the fp32 -25.0, which lies exactly
+    halfway between the codes -24 (0xDC, 1.100b x 2^4) and -26 (0xDD,
+    1.101b x 2^4): ties go to the even mantissa, 0xDC. Exact division gives
+    -25.0000004257..., past the midpoint, hence -26 (0xDD)."""
+    assert int(f8.quantize(torch.tensor([-17.5], dtype=torch.float32), 0.7)[0]) == 0xDC
+    assert int(f8.quantize(torch.tensor([17.5], dtype=torch.bfloat16), 0.7)[0]) == 0x5C
+    assert dividing_quantizer(torch.tensor([-17.5]), 0.7)[0] == 0xDD
+
+
+def dividing_quantizer(x, s):
+    """A plausible mistake: the code nearest to x / s computed exactly (fp64
+    division, then the nearest code of the fp64 quotient)."""
+    y = np.clip(x.double().numpy() / float(np.float32(s)), -448.0, 448.0)
+    table = f8.e4m3_table()
+    return [brute_force_code_f64(float(v), table) for v in y]
+
+
+def brute_force_code_f64(y, table):
+    best, best_err = None, None
+    for c in range(256):
+        v = table[c]
+        if math.isnan(v) or (v == 0.0 and math.copysign(1.0, v) != math.copysign(1.0, y)):
+            continue
+        err = abs(y - v)
+        if best is None or err < best_err or (err == best_err and (c & 1) == 0 and (best & 1) == 1):
+            best, best_err = c, err
+    return best
+
+
+def test_quantizer_non_finite_hand_worked():
+    """Reading of the non-finite inputs: a NaN keeps its sign in the NaN
+    pattern S.1111.111 (0x7F, 0xFF); infinities are clamped to +-448 (0x7E,
+    0xFE) like every other out-of-range value."""
+    pos_nan = torch.tensor([0x7FC00000], dtype=torch.int32).view(torch.float32)
+    neg_nan = torch.tensor([-0x400000], dtype=torch.int32).view(torch.float32)  # 0xFFC00000
+    x = torch.cat([pos_nan, neg_nan, torch.tensor([float("inf"), -float("inf")])])
+    assert f8.quantize(x, 0.05).tolist() == [0x7F, 0xFF, 0x7E, 0xFE]
+    assert math.isnan(f8.e4m3_value(0x7F)) and math.isnan(f8.e4m3_value(0xFF))
 
 
 def test_decode_equals_plain_oracle_on_exact_values():
