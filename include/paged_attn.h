@@ -198,6 +198,31 @@ pa_status pa_paged_attn_decode(void* out, const void* q, const void* k_cache, co
                                pa_stream_t stream);
 
 /*
+ * pa_paged_attn_decode_noalloc -- pa_paged_attn_decode for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. Same arguments, rules, results
+ * (bit for bit) and errors as pa_paged_attn_decode, without the workspace:
+ * the split-context scratch is a fixed array inside the library, one per GPU,
+ * of pa_decode_noalloc_scratch_bytes() bytes (about 8.9 MB), held until the
+ * process ends. It covers up to 65536 (sequence, query head) pairs; larger
+ * calls return PA_ERR_WORKSPACE before touching the device. The call
+ * allocates nothing: its first call on a GPU looks up that GPU's copy of the
+ * array (a symbol-address query), later calls reuse the address. `stream`
+ * must belong to the current device. Every call on one GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU (other streams, other
+ * threads) race on it: issue them one after another. Nothing needs clearing
+ * between calls (the piece counters carry a fresh tag per call).
+ */
+pa_status pa_paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                       int32_t max_context_len, float scale, pa_dtype dtype, pa_stream_t stream);
+
+/* Bytes of the per-GPU scratch array pa_paged_attn_decode_noalloc uses. */
+size_t pa_decode_noalloc_scratch_bytes(void);
+
+/*
  * pa_paged_attn_decode_ex -- pa_paged_attn_decode with an explicit number of
  * workgroups, 0 to 2048 (0 = the library's choice, the same as
  * pa_paged_attn_decode; more than 2048 is PA_ERR_INVALID_ARG). The decode

@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     library,
     paged_attn_decode,
     paged_attn_decode_fp8,
+    paged_attn_decode_noalloc,
     paged_attn_decode_store,
     paged_attn_prefill,
     prefill_workspace_bytes,

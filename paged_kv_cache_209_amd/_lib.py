@@ -47,6 +47,9 @@ SIGNATURES = {
                                     _f32, _i32, _vp, _sz, _vp]),
     "pa_paged_attn_decode_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_paged_attn_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                            _i32, _f32, _i32, _vp]),
+    "pa_decode_noalloc_scratch_bytes": (_sz, []),
     "pa_paged_attn_decode_store": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_num_workgroups": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -324,6 +327,30 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
         nb, block_tables.shape[1], int(max_context_len), float(scale), _dtype_code(q), int(num_workgroups),
         _ptr(ws), ws_bytes, _stream(q))
     _check(status, "pa_paged_attn_decode")
+    return out
+
+
+def paged_attn_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                              max_context_len: int) -> torch.Tensor:
+    """pa_paged_attn_decode_noalloc: paged_attn_decode with the library's own
+    per-GPU scratch instead of a workspace (the call allocates nothing; calls
+    on one GPU must not overlap in time)."""
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("paged_attn_decode_noalloc: q [B, Hq, D] and pools [NB, 256, Hkv, D] expected")
+    b, hq, d = q.shape
+    nb, bs, hkv, dk = k_cache.shape
+    if out.shape != q.shape or dk != d or v_cache.shape != k_cache.shape or block_tables.dim() != 2 \
+            or block_tables.shape[0] != b or context_lens.shape != (b,):
+        raise ValueError("paged_attn_decode_noalloc: shapes do not match")
+    for name, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, name, q.dtype)
+    _dev_tensor(block_tables, "block_tables", torch.int32)
+    _dev_tensor(context_lens, "context_lens", torch.int32)
+    _check(library().pa_paged_attn_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                  _ptr(block_tables), _ptr(context_lens), b, hq, hkv, d, bs, nb,
+                                                  block_tables.shape[1], int(max_context_len), float(scale),
+                                                  _dtype_code(q), _stream(q)), "pa_paged_attn_decode_noalloc")
     return out
 
 

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libpagedattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "kv_store.hip", "rope_store.hip", "decode.hip", "prefill.hip", "device_info.hip",
-           "decode_graphs.hip", "fp8_kv.hip"]
+           "decode_graphs.hip", "fp8_kv.hip", "decode_noalloc.hip"]
 # host-only C++ (no device code): built with the host compiler
 HOST_SOURCES = ["block_manager.cpp"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE]
