@@ -26,10 +26,15 @@
 //   P = 2^(S*scale*log2e - m), rounded to bf16 in registers: the S^T result
 //                 layout already is the B-operand layout of the next product
 //                 once the 32 keys of a step are taken in the order
-//                 {4q..4q+3, 16+4q..16+4q+3} for lane group q.
+//                 {4q..4q+3, 16+4q..16+4q+3} for lane group q. The row sums
+//                 add the same rounded weights with v_dot2 (two per
+//                 instruction) and are summed over the column's lane groups
+//                 once per segment.
 //   O^T += V^T P^T: A = V^T fragments read with ds_read_b64_tr_b16 from the
 //                 row-major V tile (the LDS transpose read hands each lane 4
 //                 consecutive keys of one head dim), B = P^T.
+// The LDS operand reads of each 16-key (QK) or 32-key (PV) step are issued
+// together ahead of its MFMAs.
 // K/V tiles are staged in LDS by direct-to-LDS loads (no register round
 // trip), in a swizzled layout, double-buffered so the next tile streams in
 // while the current one is used; all waves of the workgroup share them. Rows
@@ -43,7 +48,6 @@ namespace pa {
 
 namespace {
 
-constexpr int kRowsPerWave = 32;
 constexpr float kEmptyMaxP = -1.0e30f;
 constexpr float kSlack = 8.0f;
 constexpr int kNonTemporal = 2;  // cache-policy operand of direct-to-LDS loads: streaming
@@ -157,8 +161,11 @@ __device__ __forceinline__ int owner_of_unit(int64_t u, int64_t U, int64_t G) {
 
 // Where the rows of a key tile come from: the pool (through the block table)
 // for positions below c, the call's k/v for the new tokens.
-template <int D, int NT, int KT>
+template <int D_, int NT_, int KT_>
 struct TileSrc {
+  static constexpr int D = D_;
+  static constexpr int NT = NT_;
+  static constexpr int KT = KT_;
   const bf16_t* kpool;
   const bf16_t* vpool;
   const bf16_t* kg;
@@ -198,13 +205,13 @@ struct TileSrc {
 // base plus the precomputed lane offsets; a tile that straddles the two, or
 // runs past the last key (its rows re-read the last key), resolves each
 // lane's row on its own.
-template <int D, int NT, int KT>
-__device__ __forceinline__ void issue_tile(TileSrc<D, NT, KT>& t, int kt, char* stage,
-                                           const int (&krow)[KT * PShape<D, KT>::kPieces / NT],
-                                           const int (&kgo)[KT * PShape<D, KT>::kPieces / NT],
-                                           const int (&vgo)[KT * PShape<D, KT>::kPieces / NT], int tid,
-                                           int wave) {
-  constexpr int kIters = KT * PShape<D, KT>::kPieces / NT;
+template <class Src>
+__device__ __forceinline__ void issue_tile(Src& t, int kt, char* stage, const int* krow, const int* kgo,
+                                           const int* vgo, int tid, int wave) {
+  constexpr int D = Src::D;
+  constexpr int NT = Src::NT;
+  constexpr int KT = Src::KT;
+  constexpr int kIters = KT * PShape<D, KT>::kPieces / NT;  // one 16-byte piece per thread and iteration
   constexpr int TB = PShape<D, KT>::kTileBytes;
   const int k0 = kt * KT;
   char* kdst = stage;
@@ -352,22 +359,26 @@ __device__ __forceinline__ void merge_pieces(const PrefillArgs& a, bf16_t* outp,
 // on MI355X, four such workgroups per CU stream 8% faster than two with
 // 64-key tiles (more waves, and more loads in flight per CU), while one or
 // two workgroups with deeper pipelines are slower.
-template <int WM>
+template <int ROWS>
 constexpr int prefill_stages() {
-  return WM >= 8 ? 3 : 2;
+  return ROWS >= 256 ? 3 : 2;
 }
-template <int WM>
+template <int WM, int ROWS>
 constexpr int prefill_workgroups_per_cu() {
-  return WM >= 8 ? 1 : (WM == 1 ? 4 : 2);
+  return ROWS >= 256 ? 1 : (WM == 1 ? 4 : 2);
 }
 
-template <int D, int WM, int KT>
-__global__ __launch_bounds__(64 * WM, prefill_workgroups_per_cu<WM>()) void paged_prefill_kernel(PrefillArgs a) {
+// WM waves per workgroup, each owning NTW 16-column MFMA tiles of query
+// rows (16 * NTW rows), so ROWS = 16 * NTW * WM rows per item.
+template <int D, int WM, int KT, int NTW>
+__global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * WM>())) void paged_prefill_kernel(
+    PrefillArgs a) {
   using S = PShape<D, KT>;
-  constexpr int ROWS = kRowsPerWave * WM;
+  constexpr int RPW = 16 * NTW;  // query rows per wave
+  constexpr int ROWS = RPW * WM;
   constexpr int NT = kWave * WM;
   constexpr int TB = S::kTileBytes;
-  constexpr int kStages = prefill_stages<WM>();
+  constexpr int kStages = prefill_stages<ROWS>();
   constexpr int kAhead = kStages - 1;  // tiles in flight while one is used
   __shared__ __attribute__((aligned(16))) char s_kv[kStages][2 * TB];
   __shared__ int s_scan[NT];
@@ -471,7 +482,6 @@ __global__ __launch_bounds__(64 * WM, prefill_workgroups_per_cu<WM>()) void page
   // scale is negative, so that max(s) * sc is the scaled maximum.
   const float sc = a.scale_log2;
   const uint32_t qflip = a.negate_q ? 0x80008000u : 0u;
-  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
   // Split-item pieces this workgroup stores (at most its first and its last
   // segment), counted at the end.
@@ -536,14 +546,14 @@ __global__ __launch_bounds__(64 * WM, prefill_workgroups_per_cu<WM>()) void page
     src.total = total_keys;
     src.win_limit = (sg.c + kTokensPerBlock - 1) / kTokensPerBlock;
     src.fill(t_lo * KT / kTokensPerBlock, lane);
-    if (t_lo < t_hi) issue_tile<D, NT, KT>(src, t_lo, s_kv[0], krow, kgo, vgo, tid, wave);
+    if (t_lo < t_hi) issue_tile(src, t_lo, s_kv[0], krow, kgo, vgo, tid, wave);
     // This wave's query columns: nt in {0,1}, column col.
-    int qrow_tok[2];   // token index j of the lane's query column (may be >= n: padding)
-    int qrow_head[2];  // query head
-    bf16x8_t qf[2][S::kDChunks];
+    int qrow_tok[NTW];   // token index j of the lane's query column (may be >= n: padding)
+    int qrow_head[NTW];  // query head
+    bf16x8_t qf[NTW][S::kDChunks];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int R = qt * ROWS + wave * kRowsPerWave + nt * 16 + col;
+    for (int nt = 0; nt < NTW; ++nt) {
+      const int R = qt * ROWS + wave * RPW + nt * 16 + col;
       const int j = R / group;
       const int g = R % group;
       qrow_tok[nt] = j;
@@ -561,75 +571,60 @@ __global__ __launch_bounds__(64 * WM, prefill_workgroups_per_cu<WM>()) void page
     // those rows (in-order completion) does not wait for them.
 #pragma unroll
     for (int i = 1; i < kAhead; ++i)
-      if (t_lo + i < t_hi) issue_tile<D, NT, KT>(src, t_lo + i, s_kv[i], krow, kgo, vgo, tid, wave);
+      if (t_lo + i < t_hi) issue_tile(src, t_lo + i, s_kv[i], krow, kgo, vgo, tid, wave);
     // Keys a query column may see: positions <= c + j, clamped to the last key.
-    int vis[2];
+    int vis[NTW];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) vis[nt] = min(sg.c + qrow_tok[nt], total_keys - 1);
+    for (int nt = 0; nt < NTW; ++nt) vis[nt] = min(sg.c + qrow_tok[nt], total_keys - 1);
     // Smallest visible-key bound over the wave's real rows (its first row):
     // a tile entirely below it needs no mask.
-    const int wave_min_vis = min(sg.c + (qt * ROWS + wave * kRowsPerWave) / group, total_keys - 1);
+    const int wave_min_vis = min(sg.c + (qt * ROWS + wave * RPW) / group, total_keys - 1);
 
-    f32x4_t acc_o[2][S::kDTiles];
-    f32x4_t lsum[2];  // row sums from an MFMA with a ones operand (all 4 entries equal)
-    float m[2];
+    f32x4_t acc_o[NTW][S::kDTiles];
+    // Row sums of the bf16-rounded weights over the lane's own keys (each
+    // lane holds 4 keys of every 16-key tile of its column), summed across
+    // the column's 4 lane groups when the segment ends.
+    float lsum[NTW];
+    float m[NTW];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NTW; ++nt) {
       m[nt] = kEmptyMaxP;
-      lsum[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      lsum[nt] = 0.0f;
 #pragma unroll
       for (int dt = 0; dt < S::kDTiles; ++dt) acc_o[nt][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    for (int kt = t_lo; kt < t_hi; ++kt) {
-      const int k0 = kt * KT;
-      const int rel = kt - t_lo;
-      const int stage = rel % kStages;
-      constexpr int L = 2 * kIters;  // loads per tile per thread
-      if constexpr (kAhead >= 2) {
-        // Tiles kt .. kt + kAhead - 1 are in flight: wait for kt, then one
-        // barrier makes tile kt complete for every wave and shows every wave
-        // is done with tile kt - 1, whose stage then takes tile kt + kAhead.
-        const int later = min(kAhead - 1, t_hi - 1 - kt);  // tiles after kt in flight
-        if (later >= 2 && kAhead >= 3) wait_vmcnt<(kAhead >= 3 ? 2 : 0) * L>();
-        else if (later >= 1) wait_vmcnt<L>();
-        else wait_vmcnt<0>();
-        __syncthreads();
-        if (kt + kAhead < t_hi)
-          issue_tile<D, NT, KT>(src, kt + kAhead, s_kv[(rel + kAhead) % kStages], krow, kgo, vgo, tid, wave);
-      } else {
-        // Issue tile kt + 1 into the other stage (every wave finished with it
-        // at the barrier ending the previous tile), then wait for tile kt.
-        if (kt + 1 < t_hi) {
-          issue_tile<D, NT, KT>(src, kt + 1, s_kv[(rel + 1) % kStages], krow, kgo, vgo, tid, wave);
-          wait_vmcnt<L>();
-        } else {
-          wait_vmcnt<0>();
-        }
-        __syncthreads();
-      }
-      const char* s_k = s_kv[stage];
-      const char* s_v = s_kv[stage] + TB;
-
-      // -- S^T = K Q^T: st[mt][nt] holds keys 16mt + 4grp + e of query column col
-      f32x4_t st[S::kMt][2];
+    // The three phases of a key tile, for one wave's rows.
+    // S^T = K Q^T: st[mt][nt] holds keys 16mt + 4grp + e of query column col.
+    // The operand reads of a 16-key step are all issued before its MFMAs,
+    // so the LDS latency is exposed once per step rather than once per read.
+    auto qk = [&](const char* s_k, f32x4_t (&st)[S::kMt][NTW]) {
 #pragma unroll
       for (int mt = 0; mt < S::kMt; ++mt) {
-        st[mt][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        st[mt][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        bf16x8_t kfrag[S::kDChunks];
 #pragma unroll
-        for (int kc = 0; kc < S::kDChunks; ++kc) {
-          const bf16x8_t kfrag = *reinterpret_cast<const bf16x8_t*>(s_k + koff[kc] + mt * 16 * RB);
-          st[mt][0] = mfma16(kfrag, qf[0][kc], st[mt][0]);
-          st[mt][1] = mfma16(kfrag, qf[1][kc], st[mt][1]);
-        }
+        for (int kc = 0; kc < S::kDChunks; ++kc)
+          kfrag[kc] = *reinterpret_cast<const bf16x8_t*>(s_k + koff[kc] + mt * 16 * RB);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) st[mt][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kc = 0; kc < S::kDChunks; ++kc)
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) st[mt][nt] = mfma16(kfrag[kc], qf[nt][kc], st[mt][nt]);
+        __builtin_amdgcn_sched_group_barrier(0x100, S::kDChunks, 0);  // the step's LDS reads first
+        __builtin_amdgcn_sched_group_barrier(0x008, S::kDChunks * NTW, 0);  // then its MFMAs
       }
-
-      // -- online softmax per query column (raw scores; sc > 0)
+    };
+    // Online softmax of a tile starting at key k0 (raw scores; sc > 0): the
+    // causal mask, the running max (refreshed only when a score passes it by
+    // 2^kSlack), and the bf16 weights as P^T operands: for key step kc2 the
+    // lane's 8 keys are {4grp..4grp+3} of S^T tile 2kc2 and the same of tile
+    // 2kc2+1. The row sums take the same bf16-rounded weights.
+    auto softmax = [&](f32x4_t (&st)[S::kMt][NTW], int k0, bf16x8_t (&pb)[NTW][S::kKc2]) {
       const bool full_tile = k0 + KT - 1 <= wave_min_vis;
       if (!full_tile) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
           for (int mt = 0; mt < S::kMt; ++mt)
 #pragma unroll
@@ -637,9 +632,9 @@ __global__ __launch_bounds__(64 * WM, prefill_workgroups_per_cu<WM>()) void page
               if (k0 + mt * 16 + grp * 4 + e > vis[nt]) st[mt][nt][e] = -INFINITY;
       }
       bool need = false;
-      float mx[2];
+      float mx[NTW];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NTW; ++nt) {
         float t = fmaxf(fmaxf(st[0][nt][0], st[0][nt][1]), fmaxf(st[0][nt][2], st[0][nt][3]));
 #pragma unroll
         for (int mt = 1; mt < S::kMt; ++mt)
@@ -655,7 +650,7 @@ __global__ __launch_bounds__(64 * WM, prefill_workgroups_per_cu<WM>()) void page
       }
       if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NTW; ++nt) {
           const float alpha = exp2_fast(m[nt] - mx[nt]);
           lsum[nt] *= alpha;
 #pragma unroll
@@ -663,11 +658,8 @@ __global__ __launch_bounds__(64 * WM, prefill_workgroups_per_cu<WM>()) void page
           m[nt] = mx[nt];
         }
       }
-      // P^T operands, bf16: for key step kc2 the lane's 8 keys are
-      // {4grp..4grp+3} of S^T tile 2kc2 and the same of tile 2kc2+1.
-      bf16x8_t pb[2][S::kKc2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NTW; ++nt) {
         const float nm = -m[nt];
 #pragma unroll
         for (int kc2 = 0; kc2 < S::kKc2; ++kc2) {
@@ -678,38 +670,85 @@ __global__ __launch_bounds__(64 * WM, prefill_workgroups_per_cu<WM>()) void page
                              pack_bf16x2(exp2_fast(fmaf(s1[0], sc, nm)), exp2_fast(fmaf(s1[1], sc, nm))),
                              pack_bf16x2(exp2_fast(fmaf(s1[2], sc, nm)), exp2_fast(fmaf(s1[3], sc, nm)))};
           pb[nt][kc2] = __builtin_bit_cast(bf16x8_t, w);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lsum[nt] = dot2_bf16(w[e], 0x3F803F80u, lsum[nt]);
         }
       }
-
-      // -- O^T += V^T P^T, and the row sums from the same bf16 P
+    };
+    // O^T += V^T P^T: V^T operands by LDS transpose reads of the row-major V tile.
+    auto pv = [&](const char* s_v, const bf16x8_t (&pb)[NTW][S::kKc2]) {
+      typedef short i16x8_t __attribute__((ext_vector_type(8)));
 #pragma unroll
       for (int kc2 = 0; kc2 < S::kKc2; ++kc2) {
+        bf16x8_t vfrag[S::kDTiles];
 #pragma unroll
         for (int dt = 0; dt < S::kDTiles; ++dt) {
-          const char* pv = s_v + voff[dt] + kc2 * 32 * RB;
-          const i16x4_t ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(pv));
-          const i16x4_t tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(pv + 16 * RB));
-          typedef short i16x8_t __attribute__((ext_vector_type(8)));
+          const char* pvp = s_v + voff[dt] + kc2 * 32 * RB;
+          const i16x4_t ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(pvp));
+          const i16x4_t tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(pvp + 16 * RB));
           const i16x8_t t8 = {ta[0], ta[1], ta[2], ta[3], tb[0], tb[1], tb[2], tb[3]};
-          const bf16x8_t vfrag = __builtin_bit_cast(bf16x8_t, t8);
-          acc_o[0][dt] = mfma16(vfrag, pb[0][kc2], acc_o[0][dt]);
-          acc_o[1][dt] = mfma16(vfrag, pb[1][kc2], acc_o[1][dt]);
+          vfrag[dt] = __builtin_bit_cast(bf16x8_t, t8);
         }
-        lsum[0] = mfma16(ones, pb[0][kc2], lsum[0]);
-        lsum[1] = mfma16(ones, pb[1][kc2], lsum[1]);
+#pragma unroll
+        for (int dt = 0; dt < S::kDTiles; ++dt)
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) acc_o[nt][dt] = mfma16(vfrag[dt], pb[nt][kc2], acc_o[nt][dt]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * S::kDTiles, 0);  // the step's LDS reads first
+        __builtin_amdgcn_sched_group_barrier(0x008, S::kDTiles * NTW, 0);  // then its MFMAs
       }
+    };
+    constexpr int L = 2 * kIters;  // loads per tile per thread
+
+    for (int kt = t_lo; kt < t_hi; ++kt) {
+      const int rel = kt - t_lo;
+      const int stage = rel % kStages;
+      if constexpr (kAhead >= 2) {
+        // Tiles kt .. kt + kAhead - 1 are in flight: wait for kt, then one
+        // barrier makes tile kt complete for every wave and shows every
+        // wave is done with tile kt - 1, whose stage then takes tile
+        // kt + kAhead.
+        const int later = min(kAhead - 1, t_hi - 1 - kt);  // tiles after kt in flight
+        if (later >= 2 && kAhead >= 3) wait_vmcnt<(kAhead >= 3 ? 2 : 0) * L>();
+        else if (later >= 1) wait_vmcnt<L>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (kt + kAhead < t_hi)
+          issue_tile(src, kt + kAhead, s_kv[(rel + kAhead) % kStages], krow, kgo, vgo, tid, wave);
+      } else {
+        // Issue tile kt + 1 into the other stage (every wave finished with
+        // it at the barrier ending the previous tile), then wait for tile kt.
+        if (kt + 1 < t_hi) {
+          issue_tile(src, kt + 1, s_kv[(rel + 1) % kStages], krow, kgo, vgo, tid, wave);
+          wait_vmcnt<L>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        __syncthreads();
+      }
+      f32x4_t st[S::kMt][NTW];
+      qk(s_kv[stage], st);
+      bf16x8_t pb[NTW][S::kKc2];
+      softmax(st, kt * KT, pb);
+      pv(s_kv[stage] + TB, pb);
       if constexpr (kAhead < 2) __syncthreads();  // the next tile overwrites the other stage
     }
 
     // ---- finish the segment: output or partial
-    float lt[2];
+    float lt[NTW];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) lt[nt] = lsum[nt][0];
+    for (int nt = 0; nt < NTW; ++nt) {
+      // the column's 4 lane groups: rows 16-apart, then halves (same order on
+      // every lane, so every lane of the column gets the same sum)
+      const LanePair r = pair_across_rows(lsum[nt]);
+      const float t = r.lo + r.hi;
+      const LanePair h = pair_across_halves(t);
+      lt[nt] = h.lo + h.hi;
+    }
     const int first_owner = owner_of_unit(real_first, U, G);
     const int n_parts = owner_of_unit(item_end - 1, U, G) - first_owner + 1;
     if (n_parts == 1) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NTW; ++nt) {
         if (qrow_tok[nt] >= sg.n) continue;
         const float inv = 1.0f / lt[nt];
         bf16_t* orow = outp + (static_cast<int64_t>(sg.start + qrow_tok[nt]) * a.num_q_heads + qrow_head[nt]) * D;
@@ -730,8 +769,8 @@ __global__ __launch_bounds__(64 * WM, prefill_workgroups_per_cu<WM>()) void page
       const int64_t slot = 2 * static_cast<int64_t>(w) + which;
       const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(a.part_out + slot * ROWS * D, ROWS * D * 4);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int row = wave * kRowsPerWave + nt * 16 + col;
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int row = wave * RPW + nt * 16 + col;
         const bool seen = lt[nt] > 0.0f;
         const float inv = seen ? 1.0f / lt[nt] : 0.0f;
 #pragma unroll
@@ -794,22 +833,26 @@ __global__ __launch_bounds__(64 * WM, prefill_workgroups_per_cu<WM>()) void page
   }
 }
 
-template <int D, int WM, int KT>
+template <int D, int WM, int KT, int NTW>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
-  paged_prefill_kernel<D, WM, KT><<<dim3(static_cast<uint32_t>(a.num_workgroups)), dim3(64 * WM), 0, stream>>>(a);
+  paged_prefill_kernel<D, WM, KT, NTW><<<dim3(static_cast<uint32_t>(a.num_workgroups)), dim3(64 * WM), 0, stream>>>(
+      a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, int32_t head_dim, hipStream_t stream) {
+  // 256-row items: 8 waves of 32 rows, one workgroup per CU; 128-row items:
+  // 4 waves of 32 rows, two per CU; 32-row items (verify): 1 wave, four per
+  // CU.
   if (a.rows_per_tile == 256) {
-    return head_dim == 128 ? launch_typed<128, 8, 64>(a, stream) : launch_typed<64, 8, 64>(a, stream);
+    return head_dim == 128 ? launch_typed<128, 8, 64, 2>(a, stream) : launch_typed<64, 8, 64, 2>(a, stream);
   }
   if (a.rows_per_tile == 128) {
-    return head_dim == 128 ? launch_typed<128, 4, 64>(a, stream) : launch_typed<64, 4, 64>(a, stream);
+    return head_dim == 128 ? launch_typed<128, 4, 64, 2>(a, stream) : launch_typed<64, 4, 64, 2>(a, stream);
   }
-  return head_dim == 128 ? launch_typed<128, 1, 32>(a, stream) : launch_typed<64, 1, 32>(a, stream);
+  return head_dim == 128 ? launch_typed<128, 1, 32, 2>(a, stream) : launch_typed<64, 1, 32, 2>(a, stream);
 }
 
 }  // namespace pa
