@@ -11,7 +11,9 @@ The timed region holds exactly --steps steps, bracketed by device
 synchronisation, with no per-kernel events inside it; one HIP event pair on
 the launch stream brackets it, and its average is the kernel's launch
 duration for the roofline. Each workload is also timed as 30 reps, each after
-a 1 GiB flush write on the same stream, for the median, min and p90.
+a sweep that reads a 1 GiB buffer on the same stream (every cache line of the
+previous rep evicted, the caches left clean), for the median, min and p90;
+the headline also after a 1 GiB overwrite (caches left dirty).
 
 Printed: one JSON line with the headline value (decode KV throughput in
 TB/s), the roofline of its kernel, the fp64 CPU oracle timed on the host on a
@@ -44,6 +46,8 @@ KERNEL_SOURCES = {
     "decode": os.path.join(ROOT, "paged_kv_cache_209_amd", "csrc", "decode.hip"),
     "decode_store": os.path.join(ROOT, "paged_kv_cache_209_amd", "csrc", "decode.hip"),
     "prefill": os.path.join(ROOT, "paged_kv_cache_209_amd", "csrc", "prefill.hip"),
+    "kv_store": os.path.join(ROOT, "paged_kv_cache_209_amd", "csrc", "kv_store.hip"),
+    "rope_store": os.path.join(ROOT, "paged_kv_cache_209_amd", "csrc", "rope_store.hip"),
 }
 
 
@@ -309,7 +313,7 @@ def run_rope_store(torch, pa, w, steps):
             "qknorm_avg_us": round(ms_norm * 1e3, 2),
             "qknorm_frac_hbm_peak": round(nbytes / (ms_norm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": nbytes, "tokens": int(q.shape[0]), "stored_tokens": stored,
-            "rope_theta": ROPE_THETA}
+            "rope_theta": ROPE_THETA, "traffic": measured_traffic("rope_store", "c3")}
 
 
 FP8_SCALE = 1.0 / 80.0  # per-pool scale: N(0,1) values stay far inside the +-448 code range
@@ -570,14 +574,22 @@ FLUSH_BYTES = 1 << 30  # larger than the 256 MB memory-side cache and every L2
 FLUSH_REPS = 30
 
 
-def flushed_reps(torch, fn, flush_buf, reps=FLUSH_REPS):
+def flushed_reps(torch, fn, flush_buf, reps=FLUSH_REPS, write=False):
     """Durations (ms) of `reps` calls of fn(i), each preceded on the same
-    stream by a write of the 1 GiB flush buffer (so no cache holds anything
-    of the previous call) and bracketed by its own HIP event pair."""
+    stream by a sweep over the 1 GiB flush buffer and bracketed by its own
+    HIP event pair. The sweep reads the buffer (a sum), so every cache line
+    of the previous call is evicted and the caches are left holding clean
+    data, as after the weight reads that precede an attention launch in a
+    model step; with write=True it overwrites the buffer instead, leaving
+    every cache full of dirty lines that a cache-allocating load must write
+    back first."""
     pairs = []
     torch.cuda.synchronize()
     for i in range(reps):
-        flush_buf.fill_(i & 0x7F)
+        if write:
+            flush_buf.fill_(float(i & 0x7F))
+        else:
+            flush_buf.sum()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -588,14 +600,15 @@ def flushed_reps(torch, fn, flush_buf, reps=FLUSH_REPS):
     return [a.elapsed_time(b) for a, b in pairs]
 
 
-def rep_stats(ms_list):
+def rep_stats(ms_list, write=False):
     """Median, min and p90 (nearest rank) of per-rep durations, in us."""
     xs = sorted(ms_list)
     n = len(xs)
     med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
     p90 = xs[min(n - 1, max(0, math.ceil(0.9 * n) - 1))]
+    how = "overwrite" if write else "read"
     return {"median_us": round(med * 1e3, 2), "min_us": round(xs[0] * 1e3, 2), "p90_us": round(p90 * 1e3, 2),
-            "reps": n, "timing": "each rep after a 1 GiB flush write on the launch stream, own event pair "
+            "reps": n, "timing": f"each rep after a 1 GiB flush ({how}) on the launch stream, own event pair "
                                  "(~3 us of event overhead included)"}
 
 
@@ -629,8 +642,9 @@ def run_c4_headline(torch, pa, w, steps, warmup, flush_buf):
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     step_ms = t_all.ms()[0] / steps
     reps = rep_stats(flushed_reps(torch, decode, flush_buf))
+    reps_w = rep_stats(flushed_reps(torch, decode, flush_buf, write=True), write=True)
     pa.check_workspace(ws)
-    return c4, {"step_ms": step_ms, "wall_ms": wall_ms, "reps": reps}
+    return c4, {"step_ms": step_ms, "wall_ms": wall_ms, "reps": reps, "reps_write": reps_w}
 
 
 def c2_secondary(torch, pa, w, steps, warmup, copies):
@@ -743,7 +757,7 @@ def main():
 
     pa.library()
     log(f"{pa.version()} on {torch.cuda.get_device_name(0)}")
-    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+    flush_buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
 
     secondary = {}
     c4_case = None
@@ -792,6 +806,7 @@ def main():
             },
             "wall_ms_per_step": round(r["wall_ms"], 5),
             "flushed_reps": r["reps"],
+            "flushed_reps_overwrite": r["reps_write"],
         }
     else:
         result = {"metric": METRIC, "value": None, "note": f"--only {args.only}"}
@@ -817,6 +832,8 @@ def main():
             "store_flushed_reps": r3["store_reps"],
             "flops": fl,
             "algorithmic_bytes": pb["total"],
+            "traffic": measured_traffic("prefill", "c3"),
+            "store_traffic": measured_traffic("kv_store", "c3"),
         }
         del c3
     if not args.skip_secondary and args.only in ("", "c3", "rope"):
@@ -841,6 +858,7 @@ def main():
             "flushed_median_frac_hbm_peak": round(pb["total"] / med / 1e9 / HBM_PEAK_GBS, 4),
             "flops": fl,
             "algorithmic_bytes": pb["total"],
+            "traffic": measured_traffic("prefill", "c5"),
         }
     if not args.skip_secondary and args.only in ("", "fp8"):
         c2f = w.config2(device="cuda:0")

@@ -89,16 +89,23 @@ __device__ __forceinline__ void store_out<bf16_t>(bf16_t* p, float x) {
   p->bits = to_bf16_bits(x);
 }
 
+// Leading tokens of every context read with cache-allocating loads. A
+// prefix cache shares blocks only at the start of contexts (a shared system
+// prompt), so those rows may be read again by other sequences of the same
+// launch and are worth keeping in the caches; every later row is read once
+// and streams past them.
+constexpr int kCachedLeadTokens = 4 * kTokensPerBlock;
+
 // Loads the lane's words of one head row: kVecs 16-byte pieces.
-template <typename T, int D>
+template <typename T, int D, bool kStream>
 __device__ __forceinline__ void load_row(const T* row, int sl, uint32_t (&w)[DecodeShape<T, D>::kWords]) {
   using S = DecodeShape<T, D>;
 #pragma unroll
   for (int v = 0; v < S::kVecs; ++v) {
-    // Streaming (non-temporal) loads: every K/V byte is used once, and on
+    // Streaming (non-temporal) loads where every K/V byte is used once: on
     // MI355X they sustain about 10% more bandwidth than cached loads.
-    const u32x4_t x =
-        __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + v * S::kVecStride + sl * S::kElemsPerVec));
+    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(row + v * S::kVecStride + sl * S::kElemsPerVec);
+    const u32x4_t x = kStream ? __builtin_nontemporal_load(p) : *p;
     w[4 * v + 0] = x[0];
     w[4 * v + 1] = x[1];
     w[4 * v + 2] = x[2];
@@ -160,7 +167,7 @@ struct Chunk {
   uint32_t ka[W], kb[W], va[W], vb[W];
 };
 
-template <typename T, int D, bool FUSED>
+template <typename T, int D, bool FUSED, bool kStream = true>
 __device__ __forceinline__ void load_chunk(Chunk<DecodeShape<T, D>::kWords>& c, const T* kpool, const T* vpool,
                                            int block, int64_t row_stride, int c0, int t_end, int ts, int sl,
                                            const T* knew, const T* vnew, int new_pos) {
@@ -190,10 +197,10 @@ __device__ __forceinline__ void load_chunk(Chunk<DecodeShape<T, D>::kWords>& c, 
       vbb = vnew;
     }
   }
-  load_row<T, D>(ka, sl, c.ka);
-  load_row<T, D>(kbb, sl, c.kb);
-  load_row<T, D>(va, sl, c.va);
-  load_row<T, D>(vbb, sl, c.vb);
+  load_row<T, D, kStream>(ka, sl, c.ka);
+  load_row<T, D, kStream>(kbb, sl, c.kb);
+  load_row<T, D, kStream>(va, sl, c.va);
+  load_row<T, D, kStream>(vbb, sl, c.vb);
 }
 
 // Block ids of a segment, one per lane, 64 at a time. Each chunk takes its id
@@ -731,6 +738,22 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
     // chunk only.
     st.reset();
     int cn = c0;
+    // Pairs whose loads lie in the context's leading rows (the ones a prefix
+    // cache may share) use cache-allocating loads, later pairs streaming ones;
+    // two loops, so that each keeps its own kind of load.
+    while (left > 2 && cn + 2 * kStride < kCachedLeadTokens) {
+      cn += kStride;
+      load_chunk<T, D, FUSED, false>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi,
+                                     ts, sl, knew, vnew, cs.last_pos);
+      consume_chunk<T, D, GT>(st, cur, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc);
+      c0 += kStride;
+      cn += kStride;
+      load_chunk<T, D, FUSED, false>(cur, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi,
+                                     ts, sl, knew, vnew, cs.last_pos);
+      consume_chunk<T, D, GT>(st, nxt, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc);
+      c0 += kStride;
+      left -= 2;
+    }
     while (left > 2) {
       cn += kStride;
       load_chunk<T, D, FUSED>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi, ts, sl,
