@@ -487,7 +487,7 @@ pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const v
   a.ws_flags = reinterpret_cast<uint32_t*>(ws + pa::kWorkspaceFlagsOff);
   a.epoch_tag = pa::next_epoch_tag();
   a.part_lse = reinterpret_cast<float*>(ws + lay.lse_off);
-  a.part_out = reinterpret_cast<float*>(ws + lay.out_off);
+  a.part_out = reinterpret_cast<uint16_t*>(ws + lay.out_off);
   (void)hipGetLastError();
   return to_status(pa::launch_prefill(a, head_dim, static_cast<hipStream_t>(stream)));
 }

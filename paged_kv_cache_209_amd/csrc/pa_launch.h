@@ -129,7 +129,8 @@ struct PrefillArgs {
   uint32_t* ws_flags;      // workspace error word (bit 0: a counter held another call's tag)
   uint64_t epoch_tag;      // this call's tag (epoch << 16)
   float* part_lse;         // [2 * num_workgroups * rows_per_tile]
-  float* part_out;         // [2 * num_workgroups * rows_per_tile * head_dim]
+  uint16_t* part_out;      // [2 * num_workgroups * rows_per_tile * head_dim]: bf16 (half of the
+                           // space the workspace layout reserves)
 };
 
 // Largest grids the prefill launcher uses for each tile height (one 8-wave

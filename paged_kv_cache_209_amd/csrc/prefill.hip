@@ -260,94 +260,160 @@ __device__ __forceinline__ void issue_tile(Src& t, int kt, char* stage, const in
   }
 }
 
-// Merges the pieces of one split item (ROWS query rows of one sequence and KV
-// head) into the output, run by the whole workgroup: row r of the result is
-// sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M), folded in piece order with a
-// running maximum M (a piece whose keys are all causally hidden from a row
-// has lse = -inf and weight 0). Piece p lives in slot 2(first_owner + p), or
+// Log-sum-exp merge of the pieces of one split item, for the query rows and
+// dims one lane holds in the MFMA output layout (rows wave*RPW + 16nt + col,
+// dims 16dt + 4grp .. +3). Row r of the result is
+// sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M): the pieces are folded one by
+// one in piece order with a running maximum M, each fold step written with
+// explicit fused multiply-adds, so that the result does not depend on which
+// workgroup merges or where the pieces come from (a piece whose keys are all
+// causally hidden from a row has lse = -inf and weight 0). A piece's partial
+// o_p is four bf16 values per dt, packed in a uint2.
+template <int DT>
+__device__ __forceinline__ void fold_piece(float& m, float& den, f32x4_t (&num)[DT], float lse,
+                                           const uint2 (&o)[DT]) {
+  if (lse == -INFINITY) return;
+  const float mn = fmaxf(m, lse);
+  const float r = m == -INFINITY ? 0.0f : exp2_fast(m - mn);
+  const float f = exp2_fast(lse - mn);
+  den = __builtin_fmaf(den, r, f);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const float v[4] = {bf16_lo(o[dt].x), bf16_hi(o[dt].x), bf16_lo(o[dt].y), bf16_hi(o[dt].y)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) num[dt][e] = __builtin_fmaf(f, v[e], num[dt][e] * r);
+  }
+  m = mn;
+}
+
+// Tagged piece counter of item (sequence seq, KV head h, query tile qt):
+// one word per query tile the longest query could have.
+__device__ __forceinline__ uint64_t* piece_counter(const PrefillArgs& a, int seq, int h, int qt, int group, int Hkv,
+                                                   int rows) {
+  const int64_t qtiles_max = (static_cast<int64_t>(a.max_q_len) * group + rows - 1) / rows;
+  return a.counters + (static_cast<int64_t>(seq) * Hkv + h) * qtiles_max + qt;
+}
+
+// A value the caller knows to be the same on every lane of the wave, moved to
+// scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint64_t u = static_cast<uint64_t>(v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Byte offset, in a piece slot, of the 16 bytes that lane `lane` of wave
+// `wave` holds for its MFMA column tile nt and dims 32c .. 32c + 31 (its
+// dt = 2c and 2c + 1 quadruples), as bf16. The slot is laid out in the
+// lanes' own order, so that each store or load instruction of a wave covers
+// 1 KB of contiguous memory.
+template <int DT, int NTW>
+__device__ __forceinline__ int piece_chunk_offset(int wave, int nt, int c, int lane) {
+  return (((wave * NTW + nt) * (DT / 2) + c) * 64 + lane) * 16;
+}
+
+// Where a split item's pieces live: piece p in slot 2(first_owner + p), or
 // 2 first_owner + 1 for the first piece when its owner's range starts inside
-// an earlier item. Each thread takes 4 dims of kRowsPerThread rows and keeps
-// the loads of kMergeBatch pieces of a group of rows in flight together.
-// With `poison` (the item's counter held another call's tag, so its pieces
-// cannot be trusted) the rows are written as NaN instead.
-template <int D, int ROWS, int NT>
-__device__ __forceinline__ void merge_pieces(const PrefillArgs& a, bf16_t* outp, int64_t first_owner, int n_parts,
-                                             bool first_in_late_slot, const SeqGeom& sg, int qt, int h, int group,
-                                             int tid, bool poison) {
-  constexpr int D4 = D / 4;
-  constexpr int kRowStep = NT / D4;
-  constexpr int kRowsPerThread = ROWS / kRowStep;
-  constexpr int kRowGroup = kRowsPerThread < 8 ? kRowsPerThread : 8;
-  constexpr int kMergeBatch = 2;
-  static_assert(ROWS % kRowStep == 0 && kRowsPerThread % kRowGroup == 0, "merge tiling");
-  const int d4 = tid % D4;
-  const int r0 = tid / D4;
+// an earlier item (that owner's first segment took slot 2 first_owner).
+struct PieceSlots {
+  int64_t first_owner;
+  int n_parts;
+  bool first_late;
+  __device__ int64_t slot(int p) const { return 2 * (first_owner + p) + (p == 0 && first_late ? 1 : 0); }
+};
+
+// Merges a split item's pieces into the output rows this lane holds. Piece
+// `own` (or none, -1) is taken from the caller's registers (own_o, own_lse:
+// its bf16 partial and log-sum-exp, as they would have been stored); the
+// other pieces are read from the workspace, kBatch of them in flight at a
+// time. With `poison` (the item's counter held another call's tag, so its
+// pieces cannot be trusted) the rows are written as NaN instead.
+template <int D, int ROWS, int NTW, int kBatch>
+__device__ __forceinline__ void merge_item_rows(const PrefillArgs& a, bf16_t* outp, const PieceSlots& ps, int own,
+                                                const uint2 (&own_o)[NTW][D / 16], const float (&own_lse)[NTW],
+                                                const SeqGeom& sg, int qt, int h, int group, int wave, int col,
+                                                int grp, bool poison) {
+  constexpr int DT = D / 16;
+  constexpr int RPW = 16 * NTW;
+  const int lane = grp * 16 + col;
+  int tok[NTW], head[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int R = qt * ROWS + wave * RPW + nt * 16 + col;
+    tok[nt] = R / group;
+    head[nt] = h * group + R % group;
+  }
   if (poison) {
     const uint32_t nan2 = pack_bf16x2(__builtin_nanf(""), __builtin_nanf(""));
-    for (int k = 0; k < kRowsPerThread; ++k) {
-      const int R = qt * ROWS + r0 + k * kRowStep;
-      const int j = R / group;
-      if (j >= sg.n) continue;
-      bf16_t* orow = outp + (static_cast<int64_t>(sg.start + j) * a.num_q_heads + h * group + R % group) * D;
-      *reinterpret_cast<uint2*>(orow + 4 * d4) = make_uint2(nan2, nan2);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      if (tok[nt] >= sg.n) continue;
+      bf16_t* orow = outp + (static_cast<int64_t>(sg.start + tok[nt]) * a.num_q_heads + head[nt]) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<uint2*>(orow + dt * 16 + grp * 4) = make_uint2(nan2, nan2);
     }
     return;
   }
-  for (int rg = 0; rg < kRowsPerThread; rg += kRowGroup) {
-    float m[kRowGroup], den[kRowGroup];
-    f32x4_t num[kRowGroup];
+  float m[NTW], den[NTW];
+  f32x4_t num[NTW][DT];
 #pragma unroll
-    for (int k = 0; k < kRowGroup; ++k) {
-      m[k] = -INFINITY;
-      den[k] = 0.0f;
-      num[k] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    for (int p0 = 0; p0 < n_parts; p0 += kMergeBatch) {
-      float lv[kMergeBatch][kRowGroup];
-      f32x4_t ov[kMergeBatch][kRowGroup];
+  for (int nt = 0; nt < NTW; ++nt) {
+    m[nt] = -INFINITY;
+    den[nt] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const int p = min(p0 + j, n_parts - 1);
-        const int64_t slot = 2 * (first_owner + p) + (p == 0 && first_in_late_slot ? 1 : 0);
-        const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(a.part_out + slot * ROWS * D, ROWS * D * 4);
+    for (int dt = 0; dt < DT; ++dt) num[nt][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // pieces [p_begin, p_end) from the workspace
+  auto fold_stored = [&](int p_begin, int p_end) {
+    for (int p0 = p_begin; p0 < p_end; p0 += kBatch) {
+      float lv[kBatch][NTW];
+      uint2 ov[kBatch][NTW][DT];
 #pragma unroll
-        for (int k = 0; k < kRowGroup; ++k) {
-          const int row = r0 + (rg + k) * kRowStep;
-          lv[j][k] = load_agent(a.part_lse + slot * ROWS + row);
-          ov[j][k] = load4_agent(pr, (row * D + 4 * d4) * 4);
-        }
-      }
+      for (int j = 0; j < kBatch; ++j) {
+        if (p0 + j >= p_end) continue;
+        // the slot is the same on every lane: keep it (and the descriptor) scalar
+        const int64_t slot = uniform64(ps.slot(p0 + j));
+        const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(a.part_out + slot * ROWS * D, ROWS * D * 2);
 #pragma unroll
-      for (int k = 0; k < kRowGroup; ++k) {
-        float mn = m[k];
+        for (int nt = 0; nt < NTW; ++nt) {
+          const int row = wave * RPW + nt * 16 + col;
+          lv[j][nt] = load_agent(a.part_lse + slot * ROWS + row);
 #pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j)
-          if (p0 + j < n_parts) mn = fmaxf(mn, lv[j][k]);
-        if (mn == -INFINITY) continue;  // no key of these pieces is visible yet
-        const float r = m[k] == -INFINITY ? 0.0f : exp2_fast(m[k] - mn);
-        den[k] *= r;
-        num[k] *= r;
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) {
-          if (p0 + j < n_parts && lv[j][k] != -INFINITY) {
-            const float f = exp2_fast(lv[j][k] - mn);
-            den[k] += f;
-            num[k] += f * ov[j][k];
+          for (int c = 0; c < DT / 2; ++c) {
+            const f32x4_t v = load4_agent(pr, piece_chunk_offset<DT, NTW>(wave, nt, c, lane));
+            const uint4 u = __builtin_bit_cast(uint4, v);
+            ov[j][nt][2 * c] = make_uint2(u.x, u.y);
+            ov[j][nt][2 * c + 1] = make_uint2(u.z, u.w);
           }
         }
-        m[k] = mn;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (p0 + j >= p_end) break;
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) fold_piece<DT>(m[nt], den[nt], num[nt], lv[j][nt], ov[j][nt]);
       }
     }
+  };
+  if (own < 0) {
+    fold_stored(0, ps.n_parts);
+  } else {
+    fold_stored(0, own);
 #pragma unroll
-    for (int k = 0; k < kRowGroup; ++k) {
-      const int R = qt * ROWS + r0 + (rg + k) * kRowStep;
-      const int j = R / group;
-      if (j >= sg.n) continue;
-      const float inv = 1.0f / den[k];
-      const uint32_t lo = pack_bf16x2(num[k][0] * inv, num[k][1] * inv);
-      const uint32_t hi = pack_bf16x2(num[k][2] * inv, num[k][3] * inv);
-      bf16_t* orow = outp + (static_cast<int64_t>(sg.start + j) * a.num_q_heads + h * group + R % group) * D;
-      *reinterpret_cast<uint2*>(orow + 4 * d4) = make_uint2(lo, hi);
+    for (int nt = 0; nt < NTW; ++nt) fold_piece<DT>(m[nt], den[nt], num[nt], own_lse[nt], own_o[nt]);
+    fold_stored(own + 1, ps.n_parts);
+  }
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    if (tok[nt] >= sg.n) continue;
+    const float inv = 1.0f / den[nt];
+    bf16_t* orow = outp + (static_cast<int64_t>(sg.start + tok[nt]) * a.num_q_heads + head[nt]) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint32_t lo = pack_bf16x2(num[nt][dt][0] * inv, num[nt][dt][1] * inv);
+      const uint32_t hi = pack_bf16x2(num[nt][dt][2] * inv, num[nt][dt][3] * inv);
+      *reinterpret_cast<uint2*>(orow + dt * 16 + grp * 4) = make_uint2(lo, hi);
     }
   }
 }
@@ -491,10 +557,19 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
   int pend_qt[2] = {0, 0};
   int64_t pend_first[2] = {0, 0};
   int64_t pend_item_first[2] = {0, 0};
+  bool first_counted = false;  // the first pending piece was counted when it was stored
+  int first_state = 0;         // (thread 0) that count: 1 completes the item, -1 foreign counter
   __shared__ int s_cnt[2];
 
   // ---- 3. Segments.
   bool first_seg = true;  // no segment with tiles done yet (its piece goes to slot 2w)
+  // A last piece merged at once (see the end of a segment): its item, and
+  // the piece itself, as it would have been stored.
+  bool merge_last = false;
+  PieceSlots last_ps{0, 0, false};
+  int last_seq = 0, last_h = 0, last_qt = 0;
+  uint2 last_o[NTW][S::kDTiles];
+  float last_lse[NTW];
   int64_t u = u_begin;
   while (u < u_end) {
     const SeqGeom sg = seq_geom(a, seq);
@@ -760,33 +835,94 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
         }
       }
     } else {
-      // Partial slot of this piece: a workgroup's first segment with tiles
-      // uses slot 2w, its last (when it has more than one) uses slot 2w + 1.
-      // A piece may hold only keys that are causally hidden from some of its
-      // rows (sum 0): such a row's partial is 0 with log-sum-exp -inf, so the
-      // merge gives it weight 0.
-      const int which = first_seg ? 0 : 1;
-      const int64_t slot = 2 * static_cast<int64_t>(w) + which;
-      const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(a.part_out + slot * ROWS * D, ROWS * D * 4);
+      // This piece's normalised partial, rounded to bf16 (the form in which
+      // pieces are stored: it halves their traffic, and the merge adds no
+      // more than the final bf16 rounding of the output), and its fp32
+      // log-sum-exp. A piece may hold only keys that are causally hidden
+      // from some of its rows (sum 0): such a row's partial is 0 with
+      // log-sum-exp -inf, so the merge gives it weight 0.
+      uint2 pw[NTW][S::kDTiles];
+      float plse[NTW];
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
-        const int row = wave * RPW + nt * 16 + col;
         const bool seen = lt[nt] > 0.0f;
         const float inv = seen ? 1.0f / lt[nt] : 0.0f;
 #pragma unroll
         for (int dt = 0; dt < S::kDTiles; ++dt)
-          store4_agent(pr, (row * D + dt * 16 + grp * 4) * 4, acc_o[nt][dt] * inv);
-        if (grp == 0) store_agent(a.part_lse + slot * ROWS + row, seen ? m[nt] + __log2f(lt[nt]) : -INFINITY);
+          pw[nt][dt] = make_uint2(pack_bf16x2(acc_o[nt][dt][0] * inv, acc_o[nt][dt][1] * inv),
+                                  pack_bf16x2(acc_o[nt][dt][2] * inv, acc_o[nt][dt][3] * inv));
+        plse[nt] = seen ? m[nt] + __log2f(lt[nt]) : -INFINITY;
       }
-      // Nothing waits for these stores here: the piece is counted when the
-      // workgroup ends. Only a range's first and last segment can be pieces.
-      const int k = pend_n[0] == 0 ? 0 : 1;
-      pend_n[k] = n_parts;
-      pend_first[k] = first_owner;
-      pend_item_first[k] = item_first;
-      pend_seq[k] = seq;
-      pend_h[k] = h;
-      pend_qt[k] = qt;
+      const PieceSlots ps{first_owner, n_parts, first_owner * U / G < item_first};
+      // On the workgroup's last segment: if every other piece of the item is
+      // counted already (typically the item's later pieces, which were the
+      // first segments of later workgroups), no other workgroup can complete
+      // the item, and this one merges it at once with its own piece taken
+      // from registers, never storing it. Otherwise the piece is stored and
+      // counted when the workgroup ends.
+      bool merged = false;
+      if (seg_end == u_end) {
+        if (tid == 0) {
+          const uint64_t v = __hip_atomic_load(piece_counter(a, seq, h, qt, group, Hkv, ROWS), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+          s_cnt[0] = (v >> 16) == (a.epoch_tag >> 16) && static_cast<int>(v & 0xFFFFu) == n_parts - 1;
+        }
+        __syncthreads();
+        merged = s_cnt[0] != 0;
+      }
+      if (merged) {  // merged after the segment loop, which ends here
+        merge_last = true;
+        last_ps = ps;
+        last_seq = seq;
+        last_h = h;
+        last_qt = qt;
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          last_lse[nt] = plse[nt];
+#pragma unroll
+          for (int dt = 0; dt < S::kDTiles; ++dt) last_o[nt][dt] = pw[nt][dt];
+        }
+        break;
+      } else {
+        // Slot of this piece: a workgroup's first segment with tiles uses
+        // slot 2w, its last (when it has more than one) uses slot 2w + 1.
+        const int which = first_seg ? 0 : 1;
+        const int64_t slot = 2 * static_cast<int64_t>(w) + which;
+        const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(a.part_out + slot * ROWS * D, ROWS * D * 2);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const int row = wave * RPW + nt * 16 + col;
+#pragma unroll
+          for (int c = 0; c < S::kDTiles / 2; ++c) {
+            const uint4 u = make_uint4(pw[nt][2 * c].x, pw[nt][2 * c].y, pw[nt][2 * c + 1].x, pw[nt][2 * c + 1].y);
+            store4_agent(pr, piece_chunk_offset<S::kDTiles, NTW>(wave, nt, c, lane), __builtin_bit_cast(f32x4_t, u));
+          }
+          if (grp == 0) store_agent(a.part_lse + slot * ROWS + row, plse[nt]);
+        }
+        // Only a range's first and last segment can be pieces. A first
+        // segment that is not the last is the end of an item that an earlier
+        // workgroup started and finishes late: its piece is counted now
+        // (after every thread's stores are complete), so that the owner of
+        // the item's first piece can find the item complete when it gets
+        // there. The count's result is only looked at when this workgroup
+        // ends. Other pieces are counted when the workgroup ends.
+        const int k = pend_n[0] == 0 ? 0 : 1;
+        pend_n[k] = n_parts;
+        pend_first[k] = first_owner;
+        pend_item_first[k] = item_first;
+        pend_seq[k] = seq;
+        pend_h[k] = h;
+        pend_qt[k] = qt;
+        if (k == 0 && seg_end < u_end) {
+          wait_vector_memory();
+          __syncthreads();
+          if (tid == 0) {
+            const int cnt = count_arrival(piece_counter(a, seq, h, qt, group, Hkv, ROWS), a.epoch_tag);
+            first_state = cnt == n_parts ? 1 : (cnt < 0 || cnt > n_parts ? -1 : 0);
+          }
+          first_counted = true;
+        }
+      }
     }
     __syncthreads();
     first_seg = false;
@@ -802,32 +938,41 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
     }
   }
 
+  if (merge_last) {
+    merge_item_rows<D, ROWS, NTW, 2>(a, outp, last_ps, static_cast<int>(w - last_ps.first_owner), last_o, last_lse,
+                                     seq_geom(a, last_seq), last_qt, last_h, group, wave, col, grp, false);
+  }
+
   // ---- 4. Count the stored pieces once every thread's stores are complete;
   // the workgroup whose count completes an item merges its pieces.
   if (pend_n[0] > 0) {
     wait_vector_memory();
     __syncthreads();
-    const int64_t qtiles_max = (static_cast<int64_t>(a.max_q_len) * group + ROWS - 1) / ROWS;
     if (tid < 2) {  // threads 0 and 1 count the two pieces (tagged counters, see pa_launch.h)
       const int n = tid == 0 ? pend_n[0] : pend_n[1];
       int state = 0;  // 1: this arrival completes the item; -1: foreign counter
-      if (n > 0) {
-        const int64_t item = static_cast<int64_t>(tid == 0 ? pend_seq[0] : pend_seq[1]) * Hkv +
-                             (tid == 0 ? pend_h[0] : pend_h[1]);
-        uint64_t* ctr = a.counters + item * qtiles_max + (tid == 0 ? pend_qt[0] : pend_qt[1]);
-        const int cnt = count_arrival(ctr, a.epoch_tag);
+      if (tid == 0 && first_counted) {
+        state = first_state;
+        if (state < 0) flag_workspace(a.ws_flags, kWorkspaceErrStaleCounter);
+      } else if (n > 0) {
+        const int cnt = count_arrival(piece_counter(a, tid == 0 ? pend_seq[0] : pend_seq[1],
+                                                    tid == 0 ? pend_h[0] : pend_h[1],
+                                                    tid == 0 ? pend_qt[0] : pend_qt[1], group, Hkv, ROWS),
+                                      a.epoch_tag);
         state = cnt == n ? 1 : (cnt < 0 || cnt > n ? -1 : 0);
         if (state < 0) flag_workspace(a.ws_flags, kWorkspaceErrStaleCounter);
       }
       s_cnt[tid] = state;
     }
     __syncthreads();
+    const uint2 none_o[NTW][S::kDTiles] = {};
+    const float none_lse[NTW] = {};
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       if (pend_n[k] > 0 && s_cnt[k] != 0) {
-        const bool late = pend_first[k] * U / G < pend_item_first[k];
-        merge_pieces<D, ROWS, NT>(a, outp, pend_first[k], pend_n[k], late, seq_geom(a, pend_seq[k]), pend_qt[k],
-                                  pend_h[k], group, tid, s_cnt[k] < 0);
+        const PieceSlots ps{pend_first[k], pend_n[k], pend_first[k] * U / G < pend_item_first[k]};
+        merge_item_rows<D, ROWS, NTW, 2>(a, outp, ps, -1, none_o, none_lse, seq_geom(a, pend_seq[k]), pend_qt[k],
+                                         pend_h[k], group, wave, col, grp, s_cnt[k] < 0);
       }
     }
   }
