@@ -202,18 +202,6 @@ __device__ __forceinline__ f32x4_t load4_agent(__amdgpu_buffer_rsrc_t r, int byt
   return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kPolicyAgent));
 }
 
-// 8-byte agent-coherent accesses (four bf16 values) through a buffer
-// descriptor, as above.
-typedef int i32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void store2_agent(__amdgpu_buffer_rsrc_t r, int byte_off, uint2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(i32x2_t{static_cast<int>(v.x), static_cast<int>(v.y)}, r, byte_off, 0,
-                                        kPolicyAgent);
-}
-__device__ __forceinline__ uint2 load2_agent(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  const i32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kPolicyAgent);
-  return make_uint2(static_cast<uint32_t>(v.x), static_cast<uint32_t>(v.y));
-}
-
 // Wait until every vector-memory operation this wave issued (stores included)
 // has completed: s_waitcnt vmcnt(0), leaving the other counters unconstrained.
 __device__ __forceinline__ void wait_vector_memory() {
