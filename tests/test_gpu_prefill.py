@@ -115,6 +115,20 @@ def test_ragged_poisoned(shape, mix):
     compare(run_prefill(c), oracle_prefill(c), torch.bfloat16)
 
 
+@pytest.mark.parametrize("cfg", ["c3", "c5"])
+def test_full_size_repeats_bit_identical(cfg):
+    """A split item is merged by whichever of its workgroups finishes last,
+    either from the workspace alone or with its own piece still in registers;
+    both fold the pieces in piece order with the same arithmetic, so repeated
+    launches on the full-size chunked-prefill and verify workloads (where
+    that choice varies from launch to launch) give the same bits."""
+    say("prefill repeats", cfg)
+    c = w.config3(device=DEV) if cfg == "c3" else w.config5(device=DEV)
+    first = run_prefill(c)
+    for _ in range(7):
+        assert torch.equal(bits(first), bits(run_prefill(c)))
+
+
 def test_block_permutation_and_repeat_bit_identical():
     say("prefill permutation")
     c = w.build_prefill_case("perm", [600, 37, 1200], [100, 5, 260], 16, 8, 128, torch.bfloat16, 5,
