@@ -310,6 +310,13 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * out          : [total_q, num_q_heads, head_dim], written.
  * workspace    : as for decode, sized by pa_prefill_workspace_bytes; used
  *                when short query chunks are split along the context.
+ * Accuracy     : fp32 scores, softmax and accumulation; the weights are
+ *                rounded to bf16 for the matrix cores (row sums taken from
+ *                the same rounded weights). Where a row's context is split
+ *                over workgroups, each piece's normalised output is kept as
+ *                bf16 (its log-sum-exp as fp32) until the pieces are
+ *                combined, in piece order, so results do not vary from run
+ *                to run.
  * Supported dtypes: PA_BF16 (PA_F32 returns PA_ERR_UNSUPPORTED).
  */
 pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const void* v,
