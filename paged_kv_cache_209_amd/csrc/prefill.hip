@@ -423,11 +423,11 @@ __device__ __forceinline__ void merge_item_rows(const PrefillArgs& a, bf16_t* ou
 // per pair, after which the next pair loads while this one is used, so the
 // waves drift apart within a pair instead of meeting at every tile (measured
 // 4% faster than three stages with a barrier per tile); the 4-wave ones (two
-// per CU) keep one tile in flight while they work on another. The 1-wave verify workgroup takes
-// 32-key tiles, two stages (32 KB), so that four fit in a CU's LDS: measured
-// on MI355X, four such workgroups per CU stream 8% faster than two with
-// 64-key tiles (more waves, and more loads in flight per CU), while one or
-// two workgroups with deeper pipelines are slower.
+// per CU) keep one tile in flight while they work on another. The 1-wave
+// verify workgroup takes 32-key tiles, two stages (32 KB), so that four fit
+// in a CU's LDS: measured on MI355X, four such workgroups per CU stream 8%
+// faster than two with 64-key tiles (more waves, and more loads in flight
+// per CU), while one or two workgroups with deeper pipelines are slower.
 template <int ROWS>
 constexpr int prefill_stages() {
   return ROWS >= 256 ? 4 : 2;
