@@ -329,6 +329,29 @@ pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const v
                                 pa_dtype dtype, void* workspace, size_t workspace_bytes,
                                 pa_stream_t stream);
 
+/*
+ * pa_paged_attn_prefill_ex -- pa_paged_attn_prefill with an explicit number
+ * of workgroups: 0 is the library's choice (the same as
+ * pa_paged_attn_prefill); a positive value is used up to the largest grid of
+ * the row tile the call gets (256 workgroups for 256-row tiles, taken when
+ * max_q_len * num_q_heads / num_kv_heads > 128; 512 for 128-row tiles; 1024
+ * for 32-row tiles), larger values are lowered to it; negative values return
+ * PA_ERR_INVALID_ARG. The key tiles of all (sequence, KV head, query tile)
+ * items are cut into num_workgroups equal contiguous shares, so an item may
+ * be split over several workgroups and merged afterwards. Results for one
+ * num_workgroups value are bit-identical from run to run; different values
+ * agree to rounding.
+ */
+pa_status pa_paged_attn_prefill_ex(void* out, const void* q, const void* k, const void* v,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_q,
+                                   int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                   pa_dtype dtype, int32_t num_workgroups, void* workspace,
+                                   size_t workspace_bytes, pa_stream_t stream);
+
 /* Workspace bytes prefill needs for these sizes (an upper bound; may be 0). */
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_q_len, int32_t max_context_len);

@@ -56,6 +56,8 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_paged_attn_prefill_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_workspace_status": (_i32, [_vp, _sz, _vp]),
     "pa_kv_store_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _vp]),
@@ -393,9 +395,10 @@ def prefill_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_
 def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
                        v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                        cu_seqlens: torch.Tensor, scale: float, max_q_len: int, max_context_len: int,
-                       workspace_tensor: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """pa_paged_attn_prefill: causal attention of the new tokens (rows of q/k/v
-    per cu_seqlens) over each sequence's cached blocks plus the new tokens."""
+                       workspace_tensor: Optional[torch.Tensor] = None, num_workgroups: int = 0) -> torch.Tensor:
+    """pa_paged_attn_prefill(_ex): causal attention of the new tokens (rows of
+    q/k/v per cu_seqlens) over each sequence's cached blocks plus the new
+    tokens; num_workgroups = 0 lets the library choose the grid."""
     if q.dim() != 3 or k_cache.dim() != 4 or context_lens.dim() != 1:
         raise ValueError("paged_attn_prefill: q [T, Hq, D], pools [NB, 256, Hkv, D], context_lens [B] expected")
     total_q, hq, d = q.shape
@@ -413,9 +416,9 @@ def paged_attn_prefill(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
     need = prefill_workspace_bytes(b, hq, d, max_q_len, max_context_len)
     ws = workspace_tensor if workspace_tensor is not None else workspace(q.device, need, "prefill", _stream(q))
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    status = library().pa_paged_attn_prefill(
+    status = library().pa_paged_attn_prefill_ex(
         _ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         _ptr(cu_seqlens), b, total_q, int(max_q_len), hq, hkv, d, bs, nb, block_tables.shape[1],
-        int(max_context_len), float(scale), _dtype_code(q), _ptr(ws), ws_bytes, _stream(q))
+        int(max_context_len), float(scale), _dtype_code(q), int(num_workgroups), _ptr(ws), ws_bytes, _stream(q))
     _check(status, "pa_paged_attn_prefill")
     return out

@@ -424,7 +424,21 @@ pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const v
                                 int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                                 float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
                                 pa_stream_t stream) {
-  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_q_heads <= 0) return PA_ERR_INVALID_ARG;
+  return pa_paged_attn_prefill_ex(out, q, k, v, k_cache, v_cache, block_tables, context_lens, cu_seqlens, num_seqs,
+                                  total_q, max_q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                  max_blocks_per_seq, max_context_len, scale, dtype, 0, workspace, workspace_bytes,
+                                  stream);
+}
+
+pa_status pa_paged_attn_prefill_ex(void* out, const void* q, const void* k, const void* v, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                   const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                   float scale, pa_dtype dtype, int32_t num_workgroups, void* workspace,
+                                   size_t workspace_bytes, pa_stream_t stream) {
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_q_heads <= 0 || num_workgroups < 0)
+    return PA_ERR_INVALID_ARG;
   const pa_status st = check_common(num_kv_heads, head_dim, block_size, num_blocks, dtype);
   if (st != PA_OK) return st;
   if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
@@ -481,7 +495,8 @@ pa_status pa_paged_attn_prefill(void* out, const void* q, const void* k, const v
   a.scale_log2 = fabsf(sl) > 1e-30f ? fabsf(sl) : 1e-30f;
   a.negate_q = sl < 0.0f ? 1 : 0;
   a.rows_per_tile = rows;
-  a.num_workgroups = static_cast<int32_t>(max_units < cap ? max_units : cap);
+  const int64_t grid = num_workgroups > 0 && num_workgroups < cap ? num_workgroups : cap;
+  a.num_workgroups = static_cast<int32_t>(max_units < grid ? max_units : grid);
   char* ws = static_cast<char*>(workspace);
   a.counters = reinterpret_cast<uint64_t*>(ws + lay.counters_off);
   a.ws_flags = reinterpret_cast<uint32_t*>(ws + pa::kWorkspaceFlagsOff);

@@ -153,6 +153,26 @@ def test_prefill_validation(kw, expect):
     assert pre(**kw) == expect
 
 
+def pre_ex(grid, **kw):
+    a = dict(out=P, q=P, k=P, v=P, kc=P, vc=P, bt=P, cl=P, cu=P, B=2, tq=10, mq=5, hq=8, hkv=2, d=128, bs=256,
+             nb=64, mb=16, mc=4096, scale=0.088, dt=pa.PA_BF16, ws=None, wsb=0)
+    a.update(kw)
+    return pa.library().pa_paged_attn_prefill_ex(
+        a["out"], a["q"], a["k"], a["v"], a["kc"], a["vc"], a["bt"], a["cl"], a["cu"], a["B"], a["tq"], a["mq"],
+        a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mb"], a["mc"], a["scale"], a["dt"], grid, a["ws"], a["wsb"],
+        None)
+
+
+def test_prefill_ex_grid_argument():
+    """A negative grid is rejected before anything else; 0 and positive grids
+    pass to the same checks as pa_paged_attn_prefill (here: no workspace)."""
+    assert pre_ex(-1) == INVALID
+    assert pre_ex(-1, B=0) == INVALID
+    assert pre_ex(0) == WS and pre_ex(7) == WS and pre_ex(100000) == WS
+    assert pre_ex(3, B=0) == pa.PA_OK
+    assert pre_ex(3, dt=pa.PA_F32) == UNSUP
+
+
 def test_prefill_empty_is_noop_and_workspace_sizing():
     assert pre(tq=0, out=None, q=None, k=None, v=None) == pa.PA_OK
     assert pre(B=0) == pa.PA_OK

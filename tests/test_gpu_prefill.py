@@ -129,6 +129,48 @@ def test_full_size_repeats_bit_identical(cfg):
         assert torch.equal(bits(first), bits(run_prefill(c)))
 
 
+# Row-tile kinds the launcher picks from max_q_len * group: 256-row tiles
+# (8 waves), 128-row tiles (4 waves) and 32-row tiles (1 wave).
+GRID_CASES = {
+    "rows256": ([2000, 300, 0, 1500, 777], [300, 129, 200, 64, 1], 16, 8),
+    "rows128": ([1800, 0, 900, 3000], [64, 40, 1, 17], 16, 8),
+    "rows32": ([2500, 130, 4000, 0, 700], [5, 8, 3, 7, 1], 32, 8),
+}
+_grid_refs = {}
+
+
+def _grid_case(kind):
+    cached, new, hq, hkv = GRID_CASES[kind]
+    c = poisoned(w.build_prefill_case(f"grid_{kind}", cached, new, hq, hkv, 128, torch.bfloat16, 33,
+                                      with_slots=False))
+    if kind not in _grid_refs:
+        _grid_refs[kind] = oracle_prefill(c)
+    return c, _grid_refs[kind]
+
+
+@pytest.mark.parametrize("kind", list(GRID_CASES))
+@pytest.mark.parametrize("grid", [1, 2, 3, 7, 50, 131, 1000])
+def test_split_items_at_grid_sizes(kind, grid):
+    """The split-item protocol (a piece stored and counted when its range's
+    first segment ends or when the workgroup ends, or merged at once from
+    registers when the other pieces are in; merges of up to many pieces) at
+    many grid sizes and all three row-tile kinds: every row against the
+    oracle, and a second launch bit-identical to the first."""
+    say("prefill grid", kind, grid)
+    c, ref = _grid_case(kind)
+    q = to_dev(c.q)
+    args = (to_dev(c.k), to_dev(c.v), to_dev(c.k_cache), to_dev(c.v_cache), to_dev(c.block_tables),
+            to_dev(c.context_lens), to_dev(c.cu_seqlens), c.scale, c.max_q_len, c.max_context_len)
+    outs = []
+    for _ in range(2):
+        out = torch.empty_like(q)
+        pa.paged_attn_prefill(out, q, *args, num_workgroups=grid)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(bits(outs[0]), bits(outs[1]))
+    compare(outs[0], ref, torch.bfloat16)
+
+
 def test_block_permutation_and_repeat_bit_identical():
     say("prefill permutation")
     c = w.build_prefill_case("perm", [600, 37, 1200], [100, 5, 260], 16, 8, 128, torch.bfloat16, 5,
