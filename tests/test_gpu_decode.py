@@ -75,6 +75,21 @@ def test_ragged_poisoned(shape, workgroups):
     compare(out, ref, dtype)
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_zero_negative_and_large_scale(scale, dtype):
+    """The softmax scale as the caller gives it: 0 (every weight 1: the mean
+    of V over the context, the oracle's closed form P5), negative (the scores
+    flip sign) and large (sharp weights, the running max moves often); split
+    and unsplit launches against the oracle."""
+    say("decode scale", scale, dtype)
+    c = ragged_case(11, [1, 40, 300, 777, 2100], 8, 2, 128, dtype, poison=True)
+    c.scale = scale
+    ref = oracle.paged_attn_decode(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, scale)
+    for wg in (0, 1, 50):
+        compare(run_decode(c, wg), ref, dtype)
+
+
 def test_config2_full():
     say("decode c2 full")
     c = w.config2()

@@ -171,6 +171,27 @@ def test_split_items_at_grid_sizes(kind, grid):
     compare(outs[0], ref, torch.bfloat16)
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
+def test_zero_negative_and_large_scale(scale):
+    """Prefill with the scale as the caller gives it: 0 (every visible key
+    weighs 1: the causal mean of V), negative (the library negates q and
+    keeps a positive factor) and large; split and unsplit grids against the
+    oracle."""
+    say("prefill scale", scale)
+    c = poisoned(w.build_prefill_case("scale", [700, 0, 1300], [200, 64, 9], 16, 8, 128, torch.bfloat16, 44,
+                                      with_slots=False))
+    c.scale = scale
+    ref = oracle_prefill(c)
+    q = to_dev(c.q)
+    for grid in (0, 1, 40):
+        out = torch.empty_like(q)
+        pa.paged_attn_prefill(out, q, to_dev(c.k), to_dev(c.v), to_dev(c.k_cache), to_dev(c.v_cache),
+                              to_dev(c.block_tables), to_dev(c.context_lens), to_dev(c.cu_seqlens), scale,
+                              c.max_q_len, c.max_context_len, num_workgroups=grid)
+        torch.cuda.synchronize()
+        compare(out, ref, torch.bfloat16)
+
+
 def test_block_permutation_and_repeat_bit_identical():
     say("prefill permutation")
     c = w.build_prefill_case("perm", [600, 37, 1200], [100, 5, 260], 16, 8, 128, torch.bfloat16, 5,
