@@ -44,6 +44,8 @@
 //     atomics are used.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -124,8 +126,9 @@ __device__ __forceinline__ float partial_dot(const uint32_t (&qw)[DecodeShape<T,
 #pragma unroll
     for (int w = 0; w < S::kWords; ++w) {
       s0 = dot2_bf16(qw[2 * w], fp8x2_to_bf16x2<false>(kw[w]), s0);
-      s1 = dot2_bf16(qw[2 * w + 1], fp8x2_to_bf16x2<true>(kw[w]), s1);
+      s0 = dot2_bf16(qw[2 * w + 1], fp8x2_to_bf16x2<true>(kw[w]), s0);
     }
+    return s0;  // one chain: the 8 (row, head) chains of a chunk give the overlap
   } else if constexpr (Elem<T>::kBytes == 2) {
 #pragma unroll
     for (int w = 0; w < S::kWords; w += 2) {
@@ -203,6 +206,38 @@ __device__ __forceinline__ void load_chunk(Chunk<DecodeShape<T, D>::kWords>& c, 
   load_row<T, D, kStream>(vbb, sl, c.vb);
 }
 
+// Loads a chunk whose 16 rows all lie inside the range and none of which is
+// the call's new token (every chunk of a wave that has a later chunk in the
+// same segment): no row clamp and no new-token check, and the lane's rows sit
+// at fixed byte offsets (off_a, off_b) from the chunk's first row, so the
+// loads go through a raw buffer descriptor of the chunk's 16 rows (a scalar
+// base) with the offset as the only per-lane operand: no per-chunk vector
+// address arithmetic.
+template <typename T, int D, bool kStream>
+__device__ __forceinline__ void load_full_chunk(Chunk<DecodeShape<T, D>::kWords>& c, const T* kpool, const T* vpool,
+                                                int block, int64_t row_stride, int c0, uint32_t off_a,
+                                                uint32_t off_b) {
+  using S = DecodeShape<T, D>;
+  const int64_t r0 = static_cast<int64_t>(block) * kTokensPerBlock + (c0 % kTokensPerBlock);
+  const uint32_t bytes = static_cast<uint32_t>(kChunk * row_stride * sizeof(T));
+  const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kpool + r0 * row_stride, bytes);
+  const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vpool + r0 * row_stride, bytes);
+  // cache policy: nt (streaming) where every byte is read once
+  constexpr int kPolicy = kStream ? kPolicyStream : 0;
+  const auto row = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[S::kWords]) {
+#pragma unroll
+    for (int v = 0; v < S::kVecs; ++v) {
+      const i32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, off, v * 128, kPolicy);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[4 * v + k] = static_cast<uint32_t>(x[k]);
+    }
+  };
+  row(kr, off_a, c.ka);
+  row(kr, off_b, c.kb);
+  row(vr, off_a, c.va);
+  row(vr, off_b, c.vb);
+}
+
 // Block ids of a segment, one per lane, 64 at a time. Each chunk takes its id
 // with a lane read (no memory wait), so block-table reads never sit in the
 // in-order queue of vector loads behind the K/V stream.
@@ -259,10 +294,18 @@ __device__ __forceinline__ void q_words(const u32x4_t* sq, int g, int sl, uint32
   }
 }
 
+// fp8 pools: the lane's query words of every head of the group, held in
+// registers for a whole segment (32 VGPRs at 4 heads); the wider bf16 and
+// fp32 rows would not fit, so those kernels read them from LDS per chunk.
 template <typename T, int D, int GT>
+using QRegs = uint32_t[Elem<T>::kBytes == 1 ? GT : 1][DecodeShape<T, D>::kQWords];
+
+// One chunk: scores, the lazy max update and the p.V accumulation. kFull: all
+// 16 rows lie inside the range (va and vb are not consulted).
+template <typename T, int D, int GT, bool kFull = false>
 __device__ __forceinline__ void consume_chunk(LaneState<GT, DecodeShape<T, D>::kLaneElems>& st,
                                               const Chunk<DecodeShape<T, D>::kWords>& c, const u32x4_t* sq, int sl,
-                                              bool va, bool vb, float sc) {
+                                              bool va, bool vb, float sc, const QRegs<T, D, GT>& qr) {
   constexpr int W = DecodeShape<T, D>::kWords;
   constexpr int E = DecodeShape<T, D>::kLaneElems;
   float sa[GT], sb[GT];
@@ -270,11 +313,16 @@ __device__ __forceinline__ void consume_chunk(LaneState<GT, DecodeShape<T, D>::k
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
     uint32_t qw[DecodeShape<T, D>::kQWords];
-    q_words<T, D>(sq, g, sl, qw);
+    if constexpr (Elem<T>::kBytes == 1) {
+#pragma unroll
+      for (int k = 0; k < DecodeShape<T, D>::kQWords; ++k) qw[k] = qr[g][k];
+    } else {
+      q_words<T, D>(sq, g, sl, qw);
+    }
     const float da = sum8(partial_dot<T, D>(qw, c.ka));
     const float db = sum8(partial_dot<T, D>(qw, c.kb));
-    sa[g] = va ? da * sc : -INFINITY;
-    sb[g] = vb ? db * sc : -INFINITY;
+    sa[g] = kFull || va ? da * sc : -INFINITY;
+    sb[g] = kFull || vb ? db * sc : -INFINITY;
     need |= fmaxf(sa[g], sb[g]) > st.m[g] + kStaleMaxSlack;
   }
   if (__builtin_amdgcn_ballot_w64(need)) {
@@ -291,15 +339,17 @@ __device__ __forceinline__ void consume_chunk(LaneState<GT, DecodeShape<T, D>::k
   if constexpr (Elem<T>::kBytes <= 2) {
     uint32_t vp[E];
     if constexpr (Elem<T>::kBytes == 1) {
-      // fp8: word w holds elements 4w .. 4w+3 of each row
+      // fp8: word w holds elements 4w .. 4w+3 of each row. The two rows'
+      // codes are interleaved first (a0 b0 a1 b1 and a2 b2 a3 b3), so that each
+      // conversion yields the (row a, row b) pair of one element directly.
 #pragma unroll
       for (int w = 0; w < W; ++w) {
-        const uint32_t a0 = fp8x2_to_bf16x2<false>(c.va[w]), a1 = fp8x2_to_bf16x2<true>(c.va[w]);
-        const uint32_t b0 = fp8x2_to_bf16x2<false>(c.vb[w]), b1 = fp8x2_to_bf16x2<true>(c.vb[w]);
-        vp[4 * w] = pair_lo(a0, b0);
-        vp[4 * w + 1] = pair_hi(a0, b0);
-        vp[4 * w + 2] = pair_lo(a1, b1);
-        vp[4 * w + 3] = pair_hi(a1, b1);
+        const uint32_t x = __builtin_amdgcn_perm(c.vb[w], c.va[w], 0x05010400u);
+        const uint32_t y = __builtin_amdgcn_perm(c.vb[w], c.va[w], 0x07030602u);
+        vp[4 * w] = fp8x2_to_bf16x2<false>(x);
+        vp[4 * w + 1] = fp8x2_to_bf16x2<true>(x);
+        vp[4 * w + 2] = fp8x2_to_bf16x2<false>(y);
+        vp[4 * w + 3] = fp8x2_to_bf16x2<true>(y);
       }
     } else {
 #pragma unroll
@@ -737,33 +787,50 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
     // the same loads in flight and the compiler's wait before it covers that
     // chunk only.
     st.reset();
+    // byte offsets of the lane's rows (ts and ts + 8) and piece in a full chunk
+    const uint32_t off_a = static_cast<uint32_t>((ts * row_stride + sl * S::kElemsPerVec) * sizeof(T));
+    const uint32_t off_b = off_a + static_cast<uint32_t>(8 * row_stride * sizeof(T));
+    QRegs<T, D, GT> qr;
+    if constexpr (Elem<T>::kBytes == 1) {
+#pragma unroll
+      for (int g = 0; g < GT; ++g) q_words<T, D>(sq, g, sl, qr[g]);
+    }
     int cn = c0;
     // Pairs whose loads lie in the context's leading rows (the ones a prefix
     // cache may share) use cache-allocating loads, later pairs streaming ones;
     // two loops, so that each keeps its own kind of load.
-    while (left > 2 && cn + 2 * kStride < kCachedLeadTokens) {
+    // Passes of two chunks while more than three remain: every chunk a pass
+    // consumes or loads then has a later chunk of the wave in the segment,
+    // so all its rows are in range and none is the new token's (full
+    // chunks). With exactly three left, one more pass whose second load is
+    // the wave's last chunk, which takes the general load (row clamp, new-
+    // token row); kept out of the loops so that they carry no branch.
+    const auto full_pass = [&](auto stream) {
+      constexpr bool kStream = decltype(stream)::value;
       cn += kStride;
-      load_chunk<T, D, FUSED, false>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi,
-                                     ts, sl, knew, vnew, cs.last_pos);
-      consume_chunk<T, D, GT>(st, cur, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc);
+      load_full_chunk<T, D, kStream>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, off_a,
+                                     off_b);
+      consume_chunk<T, D, GT, true>(st, cur, sq, sl, true, true, sc, qr);
       c0 += kStride;
       cn += kStride;
-      load_chunk<T, D, FUSED, false>(cur, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi,
-                                     ts, sl, knew, vnew, cs.last_pos);
-      consume_chunk<T, D, GT>(st, nxt, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc);
+      load_full_chunk<T, D, kStream>(cur, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, off_a,
+                                     off_b);
+      consume_chunk<T, D, GT, true>(st, nxt, sq, sl, true, true, sc, qr);
       c0 += kStride;
       left -= 2;
-    }
-    while (left > 2) {
+    };
+    while (left > 3 && cn + 2 * kStride < kCachedLeadTokens) full_pass(std::false_type{});
+    while (left > 3) full_pass(std::true_type{});
+    if (left == 3) {
       cn += kStride;
-      load_chunk<T, D, FUSED>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi, ts, sl,
-                              knew, vnew, cs.last_pos);
-      consume_chunk<T, D, GT>(st, cur, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc);
+      load_full_chunk<T, D, true>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, off_a,
+                                  off_b);
+      consume_chunk<T, D, GT, true>(st, cur, sq, sl, true, true, sc, qr);
       c0 += kStride;
       cn += kStride;
       load_chunk<T, D, FUSED>(cur, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi, ts, sl,
                               knew, vnew, cs.last_pos);
-      consume_chunk<T, D, GT>(st, nxt, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc);
+      consume_chunk<T, D, GT, true>(st, nxt, sq, sl, true, true, sc, qr);
       c0 += kStride;
       left -= 2;
     }
@@ -778,12 +845,12 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_kernel(DecodeA
     cn = two ? cn + kStride : cn;
     load_chunk<T, D, FUSED>(nxt, kpool, vpool, bw.get(cn / kTokensPerBlock, lane), row_stride, cn, cs.t_hi, ts, sl,
                             knew, vnew, cs.last_pos);
-    consume_chunk<T, D, GT>(st, cur, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc);
+    consume_chunk<T, D, GT>(st, cur, sq, sl, c0 + ts < t_end, c0 + 8 + ts < t_end, sc, qr);
     c0 += kStride;
     load_chunk<T, D, FUSED>(cur, n_kpool, n_vpool, bwn.get(n_c0 / kTokensPerBlock, lane), row_stride, n_c0, ns.t_hi,
                             ts, sl, new_row(knew_base, ns.seq, n_kvh), new_row(vnew_base, ns.seq, n_kvh),
                             ns.last_pos);
-    consume_chunk<T, D, GT>(st, nxt, sq, sl, two && c0 + ts < t_end, two && c0 + 8 + ts < t_end, sc);
+    consume_chunk<T, D, GT>(st, nxt, sq, sl, two && c0 + ts < t_end, two && c0 + 8 + ts < t_end, sc, qr);
 
     // Merge the 8 lane groups of each wave into lanes 0-7: the upper half
     // into the lower, odd rows into even ones (VALU lane swaps that hand

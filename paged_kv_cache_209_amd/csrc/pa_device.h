@@ -192,6 +192,7 @@ __device__ __forceinline__ void flag_workspace(uint32_t* flags, uint32_t bits) {
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kBufferFlags = 0x00020000;  // raw, untyped dword access
 constexpr int kPolicyAgent = 16;         // sc1: coherent at agent scope
+constexpr int kPolicyStream = 2;         // nt: streaming, read once
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufferFlags);
 }
