@@ -576,13 +576,16 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
 
   // ---- 3. Segments.
   bool first_seg = true;  // no segment with tiles done yet (its piece goes to slot 2w)
-  // A last piece merged at once (see the end of a segment): its item, and
-  // the piece itself, as it would have been stored.
+  // A last piece merged at once (see the end of a segment): its item; the
+  // piece itself, as it would have been stored, waits in LDS (the K/V stages,
+  // free by then; each wave its own words, lane-major), so that it does not
+  // occupy registers through the tile loops of every earlier segment.
   bool merge_last = false;
   PieceSlots last_ps{0, 0, false};
   int last_seq = 0, last_h = 0, last_qt = 0;
-  uint2 last_o[NTW][S::kDTiles];
-  float last_lse[NTW];
+  constexpr int kLastWords = NTW * S::kDTiles * 2 + NTW;  // bf16 words of the piece, then its lse
+  static_assert(WM * kLastWords * kWave * 4 <= static_cast<int>(sizeof(s_kv)), "last piece in LDS");
+  uint32_t* const s_last = reinterpret_cast<uint32_t*>(&s_kv[0][0]) + wave * kLastWords * kWave + lane;
   int64_t u = u_begin;
   while (u < u_end) {
     const SeqGeom sg = seq_geom(a, seq);
@@ -890,9 +893,12 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
         last_qt = qt;
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
-          last_lse[nt] = plse[nt];
 #pragma unroll
-          for (int dt = 0; dt < S::kDTiles; ++dt) last_o[nt][dt] = pw[nt][dt];
+          for (int dt = 0; dt < S::kDTiles; ++dt) {
+            s_last[((nt * S::kDTiles + dt) * 2) * kWave] = pw[nt][dt].x;
+            s_last[((nt * S::kDTiles + dt) * 2 + 1) * kWave] = pw[nt][dt].y;
+          }
+          s_last[(NTW * S::kDTiles * 2 + nt) * kWave] = __float_as_uint(plse[nt]);
         }
         break;
       } else {
@@ -951,6 +957,17 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
   }
 
   if (merge_last) {
+    // (written by this wave before it left the loop: no barrier needed)
+    uint2 last_o[NTW][S::kDTiles];
+    float last_lse[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+      for (int dt = 0; dt < S::kDTiles; ++dt)
+        last_o[nt][dt] = make_uint2(s_last[((nt * S::kDTiles + dt) * 2) * kWave],
+                                    s_last[((nt * S::kDTiles + dt) * 2 + 1) * kWave]);
+      last_lse[nt] = __uint_as_float(s_last[(NTW * S::kDTiles * 2 + nt) * kWave]);
+    }
     merge_item_rows<D, ROWS, NTW, 2>(a, outp, last_ps, static_cast<int>(w - last_ps.first_owner), last_o, last_lse,
                                      seq_geom(a, last_seq), last_qt, last_h, group, wave, col, grp, false);
   }
