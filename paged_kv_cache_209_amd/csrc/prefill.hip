@@ -460,7 +460,18 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
   constexpr int kStages = prefill_stages<ROWS>();
   constexpr bool kPaired = kStages == 4;  // tiles in pairs, one barrier per pair
   constexpr int kAhead = kPaired ? 2 : 1;  // tiles issued before the loop
-  __shared__ __attribute__((aligned(16))) char s_kv[kStages][2 * TB];
+  static_assert(kStages == (kPaired ? 4 : 2), "two stages, or four in pairs");
+  // One LDS object per stage ([K tile | V tile]), each named where it is
+  // used: the compiler's waits for direct-to-LDS loads then tell the stages
+  // apart (one alias scope per object), so the reads of one stage do not wait
+  // for the loads still filling another. With one array indexed by stage it
+  // waited for every load in flight before a tile's first LDS read, and the
+  // next tiles' loads never overlapped the work on this one. Stages 2 and 3
+  // are used by the paired 8-wave tiles only.
+  __shared__ __attribute__((aligned(16))) char s_kv0[2 * TB];
+  __shared__ __attribute__((aligned(16))) char s_kv1[2 * TB];
+  __shared__ __attribute__((aligned(16))) char s_kv2[kPaired ? 2 * TB : 16];
+  __shared__ __attribute__((aligned(16))) char s_kv3[kPaired ? 2 * TB : 16];
   __shared__ int s_wsum[WM];
   __shared__ int s_loc[2];
 
@@ -594,8 +605,14 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
   PieceSlots last_ps{0, 0, false};
   int last_seq = 0, last_h = 0, last_qt = 0;
   constexpr int kLastWords = NTW * S::kDTiles * 2 + NTW;  // bf16 words of the piece, then its lse
-  static_assert(WM * kLastWords * kWave * 4 <= static_cast<int>(sizeof(s_kv)), "last piece in LDS");
-  uint32_t* const s_last = reinterpret_cast<uint32_t*>(&s_kv[0][0]) + wave * kLastWords * kWave + lane;
+  constexpr int kLastBytes = kLastWords * kWave * 4;  // one wave's words
+  constexpr int kLastPerStage = 2 * TB / kLastBytes;  // waves whose words fit in one stage
+  static_assert(kLastPerStage >= 1 && WM <= kLastPerStage * kStages, "last piece in LDS");
+  char* const last_stage = wave < kLastPerStage       ? s_kv0
+                           : wave < 2 * kLastPerStage ? s_kv1
+                           : wave < 3 * kLastPerStage ? s_kv2
+                                                      : s_kv3;
+  uint32_t* const s_last = reinterpret_cast<uint32_t*>(last_stage + (wave % kLastPerStage) * kLastBytes) + lane;
   int64_t u = u_begin;
   while (u < u_end) {
     const SeqGeom sg = seq_geom(a, seq);
@@ -647,7 +664,7 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
     src.total = total_keys;
     src.win_limit = (sg.c + kTokensPerBlock - 1) / kTokensPerBlock;
     src.fill(t_lo * KT / kTokensPerBlock, lane);
-    if (t_lo < t_hi) issue_tile(src, t_lo, s_kv[0], krow, kgo, vgo, tid, wave);
+    if (t_lo < t_hi) issue_tile(src, t_lo, s_kv0, krow, kgo, vgo, tid, wave);
     // This wave's query columns: nt in {0,1}, column col.
     int qrow_tok[NTW];   // token index j of the lane's query column (may be >= n: padding)
     int qrow_head[NTW];  // query head
@@ -670,9 +687,8 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
     }
     // Later prologue tiles are issued after the query rows, so the wait for
     // those rows (in-order completion) does not wait for them.
-#pragma unroll
-    for (int i = 1; i < kAhead; ++i)
-      if (t_lo + i < t_hi) issue_tile(src, t_lo + i, s_kv[i], krow, kgo, vgo, tid, wave);
+    if constexpr (kAhead > 1)
+      if (t_lo + 1 < t_hi) issue_tile(src, t_lo + 1, s_kv1, krow, kgo, vgo, tid, wave);
     // Keys a query column may see: positions <= c + j, clamped to the last key.
     int vis[NTW];
 #pragma unroll
@@ -699,7 +715,7 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
     // S^T = K Q^T: st[mt][nt] holds keys 16mt + 4grp + e of query column col.
     // The operand reads of a 16-key step are all issued before its MFMAs,
     // so the LDS latency is exposed once per step rather than once per read.
-    auto qk = [&](const char* s_k, f32x4_t (&st)[S::kMt][NTW]) {
+    auto qk = [&](const char* s_k, f32x4_t (&st)[S::kMt][NTW]) __attribute__((always_inline)) {
 #pragma unroll
       for (int mt = 0; mt < S::kMt; ++mt) {
         bf16x8_t kfrag[S::kDChunks];
@@ -721,7 +737,7 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
     // 2^kSlack), and the bf16 weights as P^T operands: for key step kc2 the
     // lane's 8 keys are {4grp..4grp+3} of S^T tile 2kc2 and the same of tile
     // 2kc2+1. The row sums take the same bf16-rounded weights.
-    auto softmax = [&](f32x4_t (&st)[S::kMt][NTW], int k0, bf16x8_t (&pb)[NTW][S::kKc2]) {
+    auto softmax = [&](f32x4_t (&st)[S::kMt][NTW], int k0, bf16x8_t (&pb)[NTW][S::kKc2]) __attribute__((always_inline)) {
       const bool full_tile = k0 + KT - 1 <= wave_min_vis;
       if (!full_tile) {
 #pragma unroll
@@ -777,7 +793,7 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
       }
     };
     // O^T += V^T P^T: V^T operands by LDS transpose reads of the row-major V tile.
-    auto pv = [&](const char* s_v, const bf16x8_t (&pb)[NTW][S::kKc2]) {
+    auto pv = [&](const char* s_v, const bf16x8_t (&pb)[NTW][S::kKc2]) __attribute__((always_inline)) {
       typedef short i16x8_t __attribute__((ext_vector_type(8)));
 #pragma unroll
       for (int kc2 = 0; kc2 < S::kKc2; ++kc2) {
@@ -800,37 +816,49 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
     };
     constexpr int L = 2 * kIters;  // loads per tile per thread
 
-    for (int kt = t_lo; kt < t_hi; ++kt) {
-      const int rel = kt - t_lo;
-      const int stage = rel % kStages;
-      if constexpr (kPaired) {
-        // At a pair's first tile, tiles kt and kt + 1 are the only ones in
-        // flight: wait for both, then one barrier makes them complete for
-        // every wave and shows every wave is done with the previous pair,
-        // whose stages then take tiles kt + 2 and kt + 3.
-        if ((rel & 1) == 0) {
-          wait_vmcnt<0>();
-          __syncthreads();
-          if (kt + 2 < t_hi) issue_tile(src, kt + 2, s_kv[(rel + 2) % kStages], krow, kgo, vgo, tid, wave);
-          if (kt + 3 < t_hi) issue_tile(src, kt + 3, s_kv[(rel + 3) % kStages], krow, kgo, vgo, tid, wave);
-        }
-      } else {
-        // Issue tile kt + 1 into the other stage (every wave finished with
-        // it at the barrier ending the previous tile), then wait for tile kt.
+    // One key tile of this wave's rows from stage `stg`.
+    auto tile = [&](int kt, const char* stg) __attribute__((always_inline)) {
+      f32x4_t st[S::kMt][NTW];
+      qk(stg, st);
+      bf16x8_t pb[NTW][S::kKc2];
+      softmax(st, kt * KT, pb);
+      pv(stg + TB, pb);
+    };
+    if constexpr (kPaired) {
+      // At a pair's start its two tiles are the only loads in flight: wait
+      // for both, then one barrier makes them complete for every wave and
+      // shows every wave is done with the previous pair, whose stages then
+      // take the next two tiles. Stages 0/1 and 2/3 alternate.
+      auto pair = [&](int kt, const char* use0, const char* use1, char* next0, char* next1) __attribute__((always_inline)) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (kt + 2 < t_hi) issue_tile(src, kt + 2, next0, krow, kgo, vgo, tid, wave);
+        if (kt + 3 < t_hi) issue_tile(src, kt + 3, next1, krow, kgo, vgo, tid, wave);
+        tile(kt, use0);
+        if (kt + 1 < t_hi) tile(kt + 1, use1);
+      };
+      for (int kt = t_lo; kt < t_hi; kt += 4) {
+        pair(kt, s_kv0, s_kv1, s_kv2, s_kv3);
+        if (kt + 2 < t_hi) pair(kt + 2, s_kv2, s_kv3, s_kv0, s_kv1);
+      }
+    } else {
+      // Issue the next tile into the other stage (every wave finished with
+      // it at the barrier ending the previous tile), then wait for this one.
+      auto step = [&](int kt, const char* use, char* next) __attribute__((always_inline)) {
         if (kt + 1 < t_hi) {
-          issue_tile(src, kt + 1, s_kv[(rel + 1) % kStages], krow, kgo, vgo, tid, wave);
+          issue_tile(src, kt + 1, next, krow, kgo, vgo, tid, wave);
           wait_vmcnt<L>();
         } else {
           wait_vmcnt<0>();
         }
         __syncthreads();
+        tile(kt, use);
+        __syncthreads();  // the next tile overwrites this stage
+      };
+      for (int kt = t_lo; kt < t_hi; kt += 2) {
+        step(kt, s_kv0, s_kv1);
+        if (kt + 1 < t_hi) step(kt + 1, s_kv1, s_kv0);
       }
-      f32x4_t st[S::kMt][NTW];
-      qk(s_kv[stage], st);
-      bf16x8_t pb[NTW][S::kKc2];
-      softmax(st, kt * KT, pb);
-      pv(s_kv[stage] + TB, pb);
-      if constexpr (!kPaired) __syncthreads();  // the next tile overwrites the other stage
     }
 
     // ---- finish the segment: output or partial
