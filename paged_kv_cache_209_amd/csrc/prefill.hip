@@ -428,6 +428,17 @@ __device__ __forceinline__ void merge_item_rows(const PrefillArgs& a, bf16_t* ou
   }
 }
 
+// A workgroup barrier without the memory fence of __syncthreads(). With
+// direct-to-LDS loads in flight that fence makes the compiler wait for all
+// of them (vmcnt 0), the next tile's included; the two-stage tile loop
+// instead waits for its own tile explicitly before the barrier, and every
+// LDS read is consumed (waited for) before its wave reaches the next one.
+__device__ __forceinline__ void tile_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // LDS stages of [K tile | V tile] per workgroup: the 8-wave workgroup (one
 // per CU) works its 64-key tiles in pairs, four stages (128 KB): one barrier
 // per pair, after which the next pair loads while this one is used, so the
@@ -844,6 +855,14 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
     } else {
       // Issue the next tile into the other stage (every wave finished with
       // it at the barrier ending the previous tile), then wait for this one.
+      // The 4-wave tiles meet at fence-free barriers, so the next tile's
+      // loads stay in flight (C3's rows on 128-row tiles: 90 -> 72-77 us);
+      // the 1-wave verify tile keeps __syncthreads(), whose wait for every
+      // load in flight measured 2% faster on a 5 GB verify.
+      auto barrier = [&]() __attribute__((always_inline)) {
+        if constexpr (WM > 1) tile_barrier();
+        else __syncthreads();
+      };
       auto step = [&](int kt, const char* use, char* next) __attribute__((always_inline)) {
         if (kt + 1 < t_hi) {
           issue_tile(src, kt + 1, next, krow, kgo, vgo, tid, wave);
@@ -851,9 +870,9 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
         } else {
           wait_vmcnt<0>();
         }
-        __syncthreads();
+        barrier();
         tile(kt, use);
-        __syncthreads();  // the next tile overwrites this stage
+        barrier();  // the next tile overwrites this stage
       };
       for (int kt = t_lo; kt < t_hi; kt += 2) {
         step(kt, s_kv0, s_kv1);
