@@ -308,7 +308,10 @@ __device__ __forceinline__ void consume_chunk(LaneState<GT, DecodeShape<T, D>::k
                                               bool va, bool vb, float sc, const QRegs<T, D, GT>& qr) {
   constexpr int W = DecodeShape<T, D>::kWords;
   constexpr int E = DecodeShape<T, D>::kLaneElems;
-  float sa[GT], sb[GT];
+  // Per query head: the two rows' raw dots, and their exponents
+  // e = s - m = dot * sc - m (log2 units) against the running max, each one
+  // fused multiply-add; the lazy-max test looks at the same exponents.
+  float xa[GT], xb[GT], ea[GT], eb[GT];
   bool need = false;
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
@@ -319,21 +322,25 @@ __device__ __forceinline__ void consume_chunk(LaneState<GT, DecodeShape<T, D>::k
     } else {
       q_words<T, D>(sq, g, sl, qw);
     }
-    const float da = sum8(partial_dot<T, D>(qw, c.ka));
-    const float db = sum8(partial_dot<T, D>(qw, c.kb));
-    sa[g] = kFull || va ? da * sc : -INFINITY;
-    sb[g] = kFull || vb ? db * sc : -INFINITY;
-    need |= fmaxf(sa[g], sb[g]) > st.m[g] + kStaleMaxSlack;
+    xa[g] = sum8(partial_dot<T, D>(qw, c.ka));
+    xb[g] = sum8(partial_dot<T, D>(qw, c.kb));
+    ea[g] = kFull || va ? fmaf(xa[g], sc, -st.m[g]) : -INFINITY;
+    eb[g] = kFull || vb ? fmaf(xb[g], sc, -st.m[g]) : -INFINITY;
+    need |= fmaxf(ea[g], eb[g]) > kStaleMaxSlack;
   }
   if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-      const float mn = fmaxf(st.m[g], fmaxf(sa[g], sb[g]));
+      const float sa = kFull || va ? xa[g] * sc : -INFINITY;
+      const float sb = kFull || vb ? xb[g] * sc : -INFINITY;
+      const float mn = fmaxf(st.m[g], fmaxf(sa, sb));
       const float alpha = exp2_fast(st.m[g] - mn);
       st.l[g] *= alpha;
 #pragma unroll
       for (int j = 0; j < E; ++j) st.acc[g][j] *= alpha;
       st.m[g] = mn;
+      ea[g] = kFull || va ? fmaf(xa[g], sc, -mn) : -INFINITY;
+      eb[g] = kFull || vb ? fmaf(xb[g], sc, -mn) : -INFINITY;
     }
   }
   if constexpr (Elem<T>::kBytes <= 2) {
@@ -360,7 +367,7 @@ __device__ __forceinline__ void consume_chunk(LaneState<GT, DecodeShape<T, D>::k
     }
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-      const uint32_t pp = pack_bf16x2(exp2_fast(sa[g] - st.m[g]), exp2_fast(sb[g] - st.m[g]));
+      const uint32_t pp = pack_bf16x2(exp2_fast(ea[g]), exp2_fast(eb[g]));
       st.l[g] = dot2_bf16(pp, 0x3F803F80u, st.l[g]);  // + p_a + p_b as rounded
 #pragma unroll
       for (int j = 0; j < E; ++j) st.acc[g][j] = dot2_bf16(pp, vp[j], st.acc[g][j]);
@@ -368,8 +375,8 @@ __device__ __forceinline__ void consume_chunk(LaneState<GT, DecodeShape<T, D>::k
   } else {
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-      const float pa = exp2_fast(sa[g] - st.m[g]);
-      const float pb = exp2_fast(sb[g] - st.m[g]);
+      const float pa = exp2_fast(ea[g]);
+      const float pb = exp2_fast(eb[g]);
       st.l[g] += pa + pb;
 #pragma unroll
       for (int j = 0; j < E; ++j)
