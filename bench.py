@@ -527,8 +527,8 @@ def cpu_baseline(case, budget_s: float):
             break
     el = time.perf_counter() - t0
     return {"value": nbytes / el / 1e12, "unit": "TB/s", "cores": torch.get_num_threads(), "kind": "oracle",
-            "sample": f"{done} of the {case.num_seqs} sequences of the config-4 decode (Qwen3-8B shape, shared "
-                      f"prefix), {nbytes / 1e9:.3f} GB of algorithmic bytes, in {el:.1f} s on {cores} host cores, "
+            "sample": f"{done} of the {case.num_seqs} sequences of the Qwen3-8B-shaped decode (contexts "
+                      f"U[1024,8192], half sharing a 1024-token prefix), {nbytes / 1e9:.3f} GB of algorithmic bytes, in {el:.1f} s on {cores} host cores, "
                       "fp64",
             "block_manager_oracle_us_per_step": block_manager_oracle_step_us(64, 128, 4096, 1, 200)}
 
@@ -886,14 +886,14 @@ def main():
         base = cpu_baseline(c4_case, args.cpu_seconds)
         del c4_case
         torch.cuda.empty_cache()
-        base["c3_prefill"] = cpu_baseline_prefill(w.config3(), 5.0, "chunked-prefill (config 3)")
+        base["c3_prefill"] = cpu_baseline_prefill(w.config3(), 5.0, "chunked-prefill (8 sequences x 512 new tokens after cached prefixes)")
         if c5_case is not None:
             host5 = w.PrefillCase(c5_case.name, c5_case.q.cpu(), c5_case.k.cpu(), c5_case.v.cpu(),
                                   c5_case.k_cache.cpu(), c5_case.v_cache.cpu(), c5_case.block_tables,
                                   c5_case.context_lens, c5_case.cu_seqlens, c5_case.scale)
             del c5_case
             torch.cuda.empty_cache()
-            base["c5_verify"] = cpu_baseline_prefill(host5, 5.0, "speculative-verify (config 5)")
+            base["c5_verify"] = cpu_baseline_prefill(host5, 5.0, "speculative-verify (128 sequences x 5 draft tokens, contexts U[2048,16384])")
             del host5
         result["cpu_baseline"] = base
     print(json.dumps(result), flush=True)
