@@ -857,10 +857,10 @@ __global__ __launch_bounds__(64 * WM, (prefill_workgroups_per_cu<WM, 16 * NTW * 
       // Issue the next tile into the other stage (every wave finished with
       // it at the barrier ending the previous tile), then wait for this one.
       // The 4-wave tiles meet at fence-free barriers, so the next tile's
-      // loads stay in flight (8 x 512-token chunked prefill forced onto 128-row
-      // tiles: 90 -> 72-77 us on MI355X);
-      // the 1-wave verify tile keeps __syncthreads(), whose wait for every
-      // load in flight measured 2% faster on a 5 GB verify.
+      // loads stay in flight (an 8 x 512-token chunked prefill forced onto
+      // 128-row tiles: 90 -> 72-77 us on MI355X); the 1-wave verify tile
+      // keeps __syncthreads(), whose wait for every load in flight measured
+      // 2% faster on a 5 GB verify.
       auto barrier = [&]() __attribute__((always_inline)) {
         if constexpr (WM > 1) tile_barrier();
         else __syncthreads();
