@@ -116,6 +116,27 @@ __device__ __forceinline__ void load_row(const T* row, int sl, uint32_t (&w)[Dec
 }
 
 // Partial q.k over the lane's elements.
+// sum8 of every element of a and b, the same adds in the same order, taken
+// one butterfly step at a time across all of them.
+template <int N>
+__device__ __forceinline__ void sum8_steps(float (&a)[N], float (&b)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    a[i] += dpp_f32<kDppXor1>(a[i]);
+    b[i] += dpp_f32<kDppXor1>(b[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    a[i] += dpp_f32<kDppXor2>(a[i]);
+    b[i] += dpp_f32<kDppXor2>(b[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    a[i] += dpp_f32<kDppHalfMirror>(a[i]);
+    b[i] += dpp_f32<kDppHalfMirror>(b[i]);
+  }
+}
+
 // fp32 dot of two bf16 pairs with a zero addend: v_dot2_f32_bf16 with an
 // inline 0 (one ALU instruction, no memory access).
 __device__ __forceinline__ float dot2_bf16_zero(uint32_t a, uint32_t b) {
@@ -335,8 +356,15 @@ __device__ __forceinline__ void consume_chunk(LaneState<GT, DecodeShape<T, D>::k
     } else {
       q_words<T, D>(sq, g, sl, qw);
     }
-    xa[g] = sum8(partial_dot<T, D>(qw, c.ka));
-    xb[g] = sum8(partial_dot<T, D>(qw, c.kb));
+    xa[g] = partial_dot<T, D>(qw, c.ka);
+    xb[g] = partial_dot<T, D>(qw, c.kb);
+  }
+  // The lane-group sums, one DPP step at a time over all 2 GT dots, so that
+  // each step's adds are independent of one another (a dependent DPP read
+  // right after its VALU write costs wait states).
+  sum8_steps(xa, xb);
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
     ea[g] = kFull || va ? fmaf(xa[g], sc, -st.m[g]) : -INFINITY;
     eb[g] = kFull || vb ? fmaf(xb[g], sc, -st.m[g]) : -INFINITY;
     need |= fmaxf(ea[g], eb[g]) > kStaleMaxSlack;
